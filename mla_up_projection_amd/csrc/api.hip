@@ -1,0 +1,300 @@
+// C ABI of the fused MLA query up-projection: host-side validation, then the
+// launches. Argument meanings, layouts and error behaviour are stated in
+// include/mla_qup.h. Validation never dereferences a device pointer and makes
+// no HIP call, so every error path runs without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+Range rng(const void* p, size_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + bytes};
+}
+
+// Outputs must be disjoint from inputs and from each other.
+bool overlaps(const std::vector<Range>& outs, const std::vector<Range>& ins) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    const Range& o = outs[i];
+    if (o.hi <= o.lo) continue;
+    for (const Range& r : ins)
+      if (r.hi > r.lo && o.lo < r.hi && r.lo < o.hi) return true;
+    for (size_t j = i + 1; j < outs.size(); ++j) {
+      const Range& r = outs[j];
+      if (r.hi > r.lo && o.lo < r.hi && r.lo < o.hi) return true;
+    }
+  }
+  return false;
+}
+
+mla_status launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_EDEVICE; }
+
+// Shape checks common to forward and backward.
+mla_status check_head_shape(int32_t K, int32_t H, int32_t d_nope, int32_t d_rope) {
+  if (K <= 0 || K % 32 != 0 || H <= 0) return MLA_EINVAL;
+  if (d_nope < 0 || d_rope < 0 || (d_nope & 1) || (d_rope & 1)) return MLA_EINVAL;
+  int64_t D = (int64_t)d_nope + d_rope;
+  if (D <= 0 || D % 32 != 0) return MLA_EINVAL;
+  if ((int64_t)H * D > (int64_t)INT32_MAX / 2) return MLA_EINVAL;
+  return MLA_OK;
+}
+
+// Token format checks; max_pos receives the largest possible position.
+mla_status check_tokens(const mla_tokens& tk, int64_t* max_pos) {
+  if (tk.T < 0 || tk.T > (int64_t)INT32_MAX) return MLA_EINVAL;
+  if (tk.fmt == MLA_FMT_BSHD || tk.fmt == MLA_FMT_SBHD) {
+    if (tk.B < 1 || tk.S < 1) return MLA_EINVAL;
+    if ((int64_t)tk.B * tk.S != tk.T) return MLA_EINVAL;
+    *max_pos = tk.S - 1;
+    return MLA_OK;
+  }
+  if (tk.fmt == MLA_FMT_THD) {
+    if (tk.nseq < 1 || tk.max_seqlen < 1) return MLA_EINVAL;
+    if (tk.T > 0 && tk.cu_seqlens == nullptr) return MLA_EINVAL;
+    if (!aligned(tk.cu_seqlens, 4)) return MLA_EINVAL;
+    *max_pos = tk.max_seqlen - 1;
+    return MLA_OK;
+  }
+  return MLA_EINVAL;
+}
+
+// The cos/sin width guard: the table must hold d_rope/2 pairs per row and a
+// row for every position (the out-of-bounds cos/sin read that the Megatron
+// page's Problem section names as a NaN source).
+mla_status check_rope(const mla_rope& r, int32_t d_rope, int64_t max_pos) {
+  if (d_rope == 0) return MLA_OK;
+  if (r.cos == nullptr || r.sin == nullptr) return MLA_EINVAL;
+  if (!aligned(r.cos, 4) || !aligned(r.sin, 4)) return MLA_EINVAL;
+  if (r.pairs < d_rope / 2) return MLA_EROPE_TABLE;
+  if ((int64_t)r.rows < max_pos + 1 || r.rows < 1) return MLA_EROPE_TABLE;
+  return MLA_OK;
+}
+
+size_t rope_bytes(const mla_rope& r, int32_t d_rope) {
+  return d_rope ? (size_t)r.rows * (size_t)r.pairs * sizeof(float) : 0;
+}
+
+void fill_token_map(const mla_tokens& tk, int& fmt, int& B, int& S, const int32_t*& cu, int& nseq) {
+  fmt = tk.fmt;
+  if (tk.fmt == MLA_FMT_THD) {
+    B = 1;
+    S = (int)tk.T;
+    cu = tk.cu_seqlens;
+    nseq = tk.nseq;
+  } else {
+    B = tk.B;
+    S = tk.S;
+    cu = nullptr;
+    nseq = 0;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_EINVAL: return "MLA_EINVAL: invalid argument";
+    case MLA_EROPE_TABLE: return "MLA_EROPE_TABLE: cos/sin table too narrow or too short";
+    case MLA_EALIAS: return "MLA_EALIAS: an output overlaps an input or another output";
+    case MLA_EUNSUPPORTED: return "MLA_EUNSUPPORTED: unsupported combination";
+    case MLA_EDEVICE: return "MLA_EDEVICE: HIP launch error";
+    case MLA_EWORKSPACE: return "MLA_EWORKSPACE: workspace missing or too small";
+    default: return "unknown mla_status";
+  }
+}
+
+mla_status rope_cache_build(float* cos, float* sin, int32_t rows, int32_t d_rope, double base,
+                            const mla_yarn* yarn, void* stream) {
+  if (cos == nullptr || sin == nullptr || rows < 1 || d_rope < 2 || (d_rope & 1)) return MLA_EINVAL;
+  if (!(base > 1.0) || !isfinite(base)) return MLA_EINVAL;
+  if (!aligned(cos, 4) || !aligned(sin, 4)) return MLA_EINVAL;
+  if (yarn) {
+    if (!(yarn->factor > 0) || yarn->orig_max_pos <= 0 || !(yarn->beta_fast > 0) ||
+        !(yarn->beta_slow > 0) || !isfinite(yarn->mscale) || !isfinite(yarn->factor))
+      return MLA_EINVAL;
+  }
+  size_t bytes = (size_t)rows * (size_t)(d_rope / 2) * sizeof(float);
+  if (overlaps({rng(cos, bytes), rng(sin, bytes)}, {})) return MLA_EALIAS;
+  return launched(mla::launch_rope_cache(cos, sin, rows, d_rope, base, yarn, (hipStream_t)stream));
+}
+
+mla_status mxfp8_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld,
+                          uint8_t* codes, uint8_t* scales, void* stream) {
+  if (x_dtype != MLA_DTYPE_BF16 && x_dtype != MLA_DTYPE_FP32) return MLA_EINVAL;
+  if (rows < 0 || cols <= 0 || cols % 32 != 0 || ld < cols) return MLA_EINVAL;
+  if (rows == 0) return MLA_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return MLA_EINVAL;
+  size_t es = x_dtype == MLA_DTYPE_FP32 ? 4 : 2;
+  if (!aligned(x, 16) || ((size_t)ld * es) % 16 != 0 || !aligned(codes, 8)) return MLA_EINVAL;
+  if (rows > ((int64_t)1 << 40) || cols > ((int64_t)1 << 31)) return MLA_EINVAL;
+  size_t xbytes = ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * es;
+  if (overlaps({rng(codes, (size_t)rows * cols), rng(scales, (size_t)rows * cols / 32)},
+               {rng(x, xbytes)}))
+    return MLA_EALIAS;
+  return launched(mla::launch_mxfp8_quantize(x, x_dtype == MLA_DTYPE_FP32, rows, cols, ld, codes,
+                                             scales, (hipStream_t)stream));
+}
+
+mla_status mla_qup_fwd(const mla_qup_fwd_args* a, void* stream) {
+  if (a == nullptr) return MLA_EINVAL;
+  mla_status st = check_head_shape(a->K, a->H, a->d_nope, a->d_rope);
+  if (st) return st;
+  int64_t max_pos = 0;
+  if ((st = check_tokens(a->tokens, &max_pos))) return st;
+  if (a->x_dtype != MLA_DTYPE_BF16 && a->x_dtype != MLA_DTYPE_MXFP8) return MLA_EINVAL;
+  if (a->w_dtype != MLA_DTYPE_BF16 && a->w_dtype != MLA_DTYPE_MXFP8) return MLA_EINVAL;
+  if (a->out_dtype != MLA_DTYPE_BF16 && a->out_dtype != MLA_DTYPE_MXFP8) return MLA_EINVAL;
+  if (a->x_dtype != a->w_dtype) return MLA_EUNSUPPORTED;
+  if (a->flags & ~(int32_t)MLA_FWD_FP8_MFMA) return MLA_EINVAL;
+  const bool mx_in = a->x_dtype == MLA_DTYPE_MXFP8;
+  const bool mx_out = a->out_dtype == MLA_DTYPE_MXFP8;
+  if (mx_in && a->K % 128 != 0) return MLA_EINVAL;
+  if ((st = check_rope(a->rope, a->d_rope, max_pos))) return st;
+  const int64_t T = a->tokens.T;
+  if (T == 0) return MLA_OK;
+  if (a->x == nullptr || a->w == nullptr || a->out == nullptr) return MLA_EINVAL;
+  if (mx_in && (a->x_scales == nullptr || a->w_scales == nullptr)) return MLA_EINVAL;
+  if (mx_out && a->out_scales == nullptr) return MLA_EINVAL;
+  if (!aligned(a->x, 16) || !aligned(a->w, 16) || !aligned(a->out, 16)) return MLA_EINVAL;
+  if (a->bias && !aligned(a->bias, 2)) return MLA_EINVAL;
+
+  const int D = a->d_nope + a->d_rope;
+  const int64_t N = (int64_t)a->H * D;
+  const size_t ein = mx_in ? 1 : 2;
+  const size_t eout = mx_out ? 1 : 2;
+  std::vector<Range> ins = {rng(a->x, (size_t)T * a->K * ein), rng(a->w, (size_t)N * a->K * ein)};
+  if (mx_in) {
+    ins.push_back(rng(a->x_scales, (size_t)T * a->K / 32));
+    ins.push_back(rng(a->w_scales, (size_t)N * a->K / 32));
+  }
+  if (a->bias) ins.push_back(rng(a->bias, (size_t)N * 2));
+  if (a->d_rope) {
+    ins.push_back(rng(a->rope.cos, rope_bytes(a->rope, a->d_rope)));
+    ins.push_back(rng(a->rope.sin, rope_bytes(a->rope, a->d_rope)));
+  }
+  if (a->tokens.fmt == MLA_FMT_THD)
+    ins.push_back(rng(a->tokens.cu_seqlens, (size_t)(a->tokens.nseq + 1) * 4));
+  std::vector<Range> outs = {rng(a->out, (size_t)T * N * eout)};
+  if (mx_out) outs.push_back(rng(a->out_scales, (size_t)T * N / 32));
+  if (overlaps(outs, ins)) return MLA_EALIAS;
+
+  mla::FwdParams p{};
+  p.x = a->x;
+  p.xs = a->x_scales;
+  p.w = a->w;
+  p.ws = a->w_scales;
+  p.bias = (const uint16_t*)a->bias;
+  p.T = T;
+  p.K = a->K;
+  p.N = (int)N;
+  p.H = a->H;
+  p.D = D;
+  p.d_nope = a->d_nope;
+  p.d_rope = a->d_rope;
+  fill_token_map(a->tokens, p.fmt, p.B, p.S, p.cu, p.nseq);
+  p.cos = a->rope.cos;
+  p.sin = a->rope.sin;
+  p.rope_rows = a->d_rope ? a->rope.rows : 0;
+  p.rope_pairs = a->d_rope ? a->rope.pairs : 0;
+  p.out_mx = mx_out;
+  p.mx_fp8_mfma = (a->flags & MLA_FWD_FP8_MFMA) ? 1 : 0;
+  p.out = a->out;
+  p.out_scales = a->out_scales;
+  hipStream_t s = (hipStream_t)stream;
+  return launched(mx_in ? mla::launch_qup_fwd_mx(p, s) : mla::launch_qup_fwd_bf16(p, s));
+}
+
+static mla_status check_bwd_shapes(const mla_qup_bwd_args* a, int64_t* max_pos) {
+  if (a == nullptr) return MLA_EINVAL;
+  mla_status st = check_head_shape(a->K, a->H, a->d_nope, a->d_rope);
+  if (st) return st;
+  if ((st = check_tokens(a->tokens, max_pos))) return st;
+  if (a->dw_dtype != MLA_DTYPE_BF16 && a->dw_dtype != MLA_DTYPE_FP32) return MLA_EINVAL;
+  if (a->use_bias != 0 && a->use_bias != 1) return MLA_EINVAL;
+  return MLA_OK;
+}
+
+size_t mla_qup_bwd_workspace_size(const mla_qup_bwd_args* a) {
+  int64_t max_pos = 0;
+  if (check_bwd_shapes(a, &max_pos) != MLA_OK) return 0;
+  const int N = a->H * (a->d_nope + a->d_rope);
+  return mla::plan_bwd(a->tokens.T, N, a->K, a->use_bias != 0, a->dx != nullptr).total;
+}
+
+mla_status mla_qup_bwd(const mla_qup_bwd_args* a, void* stream) {
+  int64_t max_pos = 0;
+  mla_status st = check_bwd_shapes(a, &max_pos);
+  if (st) return st;
+  if ((st = check_rope(a->rope, a->d_rope, max_pos))) return st;
+  const int64_t T = a->tokens.T;
+  const int D = a->d_nope + a->d_rope;
+  const int N = a->H * D;
+  if (a->use_bias && a->db == nullptr) return MLA_EINVAL;
+  if (T > 0 && (a->dq == nullptr || a->x == nullptr || a->w == nullptr || a->dq_pre == nullptr))
+    return MLA_EINVAL;
+  if (!aligned(a->dq, 16) || !aligned(a->x, 16) || !aligned(a->w, 16) ||
+      !aligned(a->dq_pre, 16) || (a->dx && !aligned(a->dx, 16)) || (a->dw && !aligned(a->dw, 16)) ||
+      (a->db && !aligned(a->db, 2)))
+    return MLA_EINVAL;
+  mla::BwdPlan plan = mla::plan_bwd(T, N, a->K, a->use_bias != 0, a->dx != nullptr);
+  if (plan.total > 0) {
+    if (a->workspace == nullptr || a->workspace_bytes < plan.total) return MLA_EWORKSPACE;
+    if (!aligned(a->workspace, 256)) return MLA_EINVAL;
+  }
+  std::vector<Range> ins = {rng(a->dq, (size_t)T * N * 2), rng(a->x, (size_t)T * a->K * 2),
+                            rng(a->w, (size_t)N * a->K * 2)};
+  if (a->d_rope) {
+    ins.push_back(rng(a->rope.cos, rope_bytes(a->rope, a->d_rope)));
+    ins.push_back(rng(a->rope.sin, rope_bytes(a->rope, a->d_rope)));
+  }
+  if (a->tokens.fmt == MLA_FMT_THD)
+    ins.push_back(rng(a->tokens.cu_seqlens, (size_t)(a->tokens.nseq + 1) * 4));
+  std::vector<Range> outs = {rng(a->dq_pre, (size_t)T * N * 2)};
+  if (a->dx) outs.push_back(rng(a->dx, (size_t)T * a->K * 2));
+  if (a->dw) outs.push_back(rng(a->dw, (size_t)N * a->K * (a->dw_dtype == MLA_DTYPE_FP32 ? 4 : 2)));
+  if (a->use_bias) outs.push_back(rng(a->db, (size_t)N * 2));
+  if (plan.total) outs.push_back(rng(a->workspace, plan.total));
+  if (overlaps(outs, ins)) return MLA_EALIAS;
+
+  mla::BwdParams p{};
+  p.dq = (const uint16_t*)a->dq;
+  p.x = (const uint16_t*)a->x;
+  p.w = (const uint16_t*)a->w;
+  p.T = T;
+  p.K = a->K;
+  p.N = N;
+  p.H = a->H;
+  p.D = D;
+  p.d_nope = a->d_nope;
+  p.d_rope = a->d_rope;
+  fill_token_map(a->tokens, p.fmt, p.B, p.S, p.cu, p.nseq);
+  p.cos = a->rope.cos;
+  p.sin = a->rope.sin;
+  p.rope_rows = a->d_rope ? a->rope.rows : 0;
+  p.rope_pairs = a->d_rope ? a->rope.pairs : 0;
+  p.dq_pre = (uint16_t*)a->dq_pre;
+  p.dx = (uint16_t*)a->dx;
+  p.dw = a->dw;
+  p.dw_fp32 = a->dw_dtype == MLA_DTYPE_FP32;
+  p.use_bias = a->use_bias;
+  p.db = (uint16_t*)a->db;
+  p.workspace = a->workspace;
+  return launched(mla::launch_qup_bwd(p, plan, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+// Every launcher assumes its arguments were validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla_qup.h"
+
+namespace mla {
+
+struct FwdParams {
+  const void* x;           // bf16 [T,K] or e4m3 codes [T,K]
+  const uint8_t* xs;       // MXFP8 x scales [T,K/32]
+  const void* w;           // bf16 [N,K] or e4m3 codes [N,K]
+  const uint8_t* ws;       // MXFP8 w scales [N,K/32]
+  const uint16_t* bias;    // bf16 [N] or nullptr
+  int64_t T;
+  int K, N, H, D, d_nope, d_rope;
+  int fmt, B, S;           // BHSD output dims; THD: B = 1, S = T
+  const int32_t* cu;
+  int nseq;
+  const float* cos;
+  const float* sin;
+  int rope_rows, rope_pairs;
+  int out_mx;              // 1: MXFP8 codes + scales, 0: bf16
+  int mx_fp8_mfma;         // MXFP8 operands on the scaled FP8 MFMA (else exact bf16 MFMA)
+  void* out;
+  uint8_t* out_scales;
+};
+
+struct BwdParams {
+  const uint16_t* dq;
+  const uint16_t* x;
+  const uint16_t* w;
+  int64_t T;
+  int K, N, H, D, d_nope, d_rope;
+  int fmt, B, S;
+  const int32_t* cu;
+  int nseq;
+  const float* cos;
+  const float* sin;
+  int rope_rows, rope_pairs;
+  uint16_t* dq_pre;
+  uint16_t* dx;
+  void* dw;
+  int dw_fp32;
+  int use_bias;
+  uint16_t* db;
+  void* workspace;
+};
+
+// Workspace plan of the backward: byte offsets into the caller's workspace.
+struct BwdPlan {
+  int db_row_chunks;       // token chunks of the db partial sums
+  size_t db_off, db_bytes;
+  int dx_splits;           // reduction splits of the dX GEMM (1 = none)
+  size_t dx_off, dx_bytes;
+  size_t total;
+};
+BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx);
+
+hipError_t launch_rope_cache(float* cos, float* sin, int rows, int d_rope, double base,
+                             const mla_yarn* yarn, hipStream_t stream);
+hipError_t launch_mxfp8_quantize(const void* x, int x_fp32, int64_t rows, int64_t cols,
+                                 int64_t ld, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream);
+hipError_t launch_qup_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_qup_fwd_mx(const FwdParams& p, hipStream_t stream);
+hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& plan, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,83 @@
+// Separable MXFP8 quantization of a row-major matrix along its rows, one
+// E8M0 scale per 32 consecutive elements (OCP Microscaling Formats v1.0).
+// Forward page (file table, review thread): the standalone MXFP8 quantize
+// used for operands of the MXFP8 projection. HBM-bound: each element is read
+// once (2 or 4 bytes) and written once (1 byte + 1/32 byte of scale).
+//
+// Four consecutive lanes own one 32-element block, eight elements each
+// (one 16-byte bf16 load or two fp32 loads per lane, one 8-byte store); the
+// block amax is an integer max over |x| bit patterns reduced across the four
+// lanes with two xor-shuffles.
+#include "device_common.h"
+#include "internal.h"
+
+namespace mla {
+namespace {
+
+template <bool FP32>
+__global__ __launch_bounds__(256) void mxfp8_quant_kernel(const void* __restrict__ x, int64_t rows,
+                                                          int64_t cols, int64_t ld,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  const int64_t groups = rows * (cols / 8);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
+    const int64_t e = g * 8;
+    const int64_t row = e / cols;
+    const int64_t col = e - row * cols;
+    float v[8];
+    if (FP32) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + row * ld + col);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      const uint4 u =
+          *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + row * ld + col);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, abs_bits(v[i]));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    uint32_t c0 = 0, c1 = 0, sc;
+    if (m >= 0x7F800000u) {
+      c0 = c1 = 0x7F7F7F7Fu;
+      sc = 0xFF;
+    } else {
+      const int E = mx_block_exp(m);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c0 |= e4m3_encode(v[i], E) << (8 * i);
+        c1 |= e4m3_encode(v[4 + i], E) << (8 * i);
+      }
+      sc = (uint32_t)(E + 127);
+    }
+    *reinterpret_cast<uint2*>(codes + row * cols + col) = make_uint2(c0, c1);
+    if ((g & 3) == 0) scales[row * (cols / 32) + col / 32] = (uint8_t)sc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mxfp8_quantize(const void* x, int x_fp32, int64_t rows, int64_t cols, int64_t ld,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const int64_t groups = rows * (cols / 8);
+  int64_t blocks = (groups + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (x_fp32)
+    hipLaunchKernelGGL(mxfp8_quant_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       rows, cols, ld, codes, scales);
+  else
+    hipLaunchKernelGGL(mxfp8_quant_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       rows, cols, ld, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,199 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/mla_qup.h declares, and every validation error is returned before
+anything is enqueued (fake device addresses are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mla_up_projection_amd as m
+from mla_up_projection_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bd.LIB_PATH):
+        from mla_up_projection_amd import build
+        build.build()
+    return bd.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mla_qup.h")).read()
+    return sorted(set(re.findall(r"MLA_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(bd.FUNCTIONS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code in range(7):
+        assert m.mla_status_str(code).startswith("MLA_")
+    assert "unknown" in m.mla_status_str(99)
+
+
+def test_struct_layouts_match_c(tmp_path):
+    """sizeof/offsetof of every ABI struct as gcc lays it out == the ctypes mirror."""
+    structs = [bd.mla_tokens, bd.mla_yarn, bd.mla_rope, bd.mla_qup_fwd_args, bd.mla_qup_bwd_args]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "mla_qup.h"', "int main(void){"]
+    for s in structs:
+        lines.append(f'printf("{s.__name__} %zu\\n", sizeof({s.__name__}));')
+        for f, _ in s._fields_:
+            lines.append(f'printf("{s.__name__}.{f} %zu\\n", offsetof({s.__name__}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                  check=True).stdout.splitlines())
+    for s in structs:
+        assert int(out[s.__name__]) == ctypes.sizeof(s), s.__name__
+        for f, _ in s._fields_:
+            assert int(out[f"{s.__name__}.{f}"]) == getattr(s, f).offset, (s.__name__, f)
+
+
+# Fake, 256-byte-aligned, far-apart device addresses: validation only compares
+# and aligns them.
+BASE = 0x7F0000000000
+def addr(i, off=0):
+    return BASE + i * (1 << 36) + off
+
+
+def fwd_args(**over):
+    a = bd.mla_qup_fwd_args()
+    T, K, H, dn, dr = 256, 1536, 4, 128, 64
+    a.x, a.x_dtype = addr(1), bd.DTYPE_BF16
+    a.w, a.w_dtype = addr(2), bd.DTYPE_BF16
+    a.K, a.H, a.d_nope, a.d_rope = K, H, dn, dr
+    a.tokens.fmt, a.tokens.B, a.tokens.S, a.tokens.T = bd.FMT_BSHD, 1, T, T
+    a.rope.cos, a.rope.sin, a.rope.rows, a.rope.pairs = addr(3), addr(4), T, dr // 2
+    a.out_dtype, a.out, a.out_scales = bd.DTYPE_MXFP8, addr(5), addr(6)
+    for k, v in over.items():
+        obj = a
+        *path, last = k.split("__")
+        for p in path:
+            obj = getattr(obj, p)
+        setattr(obj, last, v)
+    return a
+
+
+def fwd(L, **over):
+    return L.mla_qup_fwd(ctypes.byref(fwd_args(**over)), None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(K=0), bd.MLA_EINVAL),
+    (dict(K=100), bd.MLA_EINVAL),
+    (dict(H=0), bd.MLA_EINVAL),
+    (dict(d_rope=63), bd.MLA_EINVAL),
+    (dict(d_nope=120), bd.MLA_EINVAL),                    # D = 184 not a multiple of 32
+    (dict(tokens__B=2), bd.MLA_EINVAL),                   # B*S != T
+    (dict(tokens__fmt=7), bd.MLA_EINVAL),
+    (dict(x=0), bd.MLA_EINVAL),
+    (dict(out=0), bd.MLA_EINVAL),
+    (dict(out_scales=0), bd.MLA_EINVAL),
+    (dict(x=addr(1, 8)), bd.MLA_EINVAL),                  # misaligned
+    (dict(out_dtype=9), bd.MLA_EINVAL),
+    (dict(x_dtype=bd.DTYPE_MXFP8), bd.MLA_EUNSUPPORTED),  # MXFP8 x with BF16 w
+    (dict(rope__pairs=31), bd.MLA_EROPE_TABLE),           # table narrower than d_rope/2
+    (dict(rope__rows=255), bd.MLA_EROPE_TABLE),           # no row for position 255
+    (dict(rope__cos=0), bd.MLA_EINVAL),
+    (dict(out=addr(1, 4096)), bd.MLA_EALIAS),             # output inside x
+    (dict(out_scales=addr(5, 64)), bd.MLA_EALIAS),        # scales inside out
+    (dict(out=addr(3)), bd.MLA_EALIAS),                   # output over the cos table
+])
+def test_fwd_validation(L, over, code):
+    assert fwd(L, **over) == code
+
+
+def test_fwd_validation_mx_and_thd(L):
+    mx = dict(x_dtype=bd.DTYPE_MXFP8, w_dtype=bd.DTYPE_MXFP8)
+    assert fwd(L, **mx) == bd.MLA_EINVAL                          # scales missing
+    assert fwd(L, **mx, x_scales=addr(7), w_scales=addr(8), K=1600) == bd.MLA_EINVAL  # K % 128
+    thd = dict(tokens__fmt=bd.FMT_THD, tokens__cu_seqlens=addr(9), tokens__nseq=2,
+               tokens__max_seqlen=200)
+    assert fwd(L, **{**thd, "tokens__nseq": 0}) == bd.MLA_EINVAL
+    assert fwd(L, **{**thd, "tokens__cu_seqlens": 0}) == bd.MLA_EINVAL
+    assert fwd(L, **{**thd, "rope__rows": 199}) == bd.MLA_EROPE_TABLE
+    assert fwd(L, **{**thd, "out": addr(9, 0)}) == bd.MLA_EALIAS
+    # zero tokens: valid, nothing enqueued (no GPU needed)
+    assert fwd(L, tokens__T=0, tokens__S=0, tokens__B=1) == bd.MLA_EINVAL  # S < 1
+    assert fwd(L, **{**thd, "tokens__T": 0}) == bd.MLA_OK
+
+
+def bwd_args(**over):
+    a = bd.mla_qup_bwd_args()
+    T, K, H, dn, dr = 256, 1536, 4, 128, 64
+    a.dq, a.x, a.w = addr(1), addr(2), addr(3)
+    a.K, a.H, a.d_nope, a.d_rope = K, H, dn, dr
+    a.tokens.fmt, a.tokens.B, a.tokens.S, a.tokens.T = bd.FMT_BSHD, 1, T, T
+    a.rope.cos, a.rope.sin, a.rope.rows, a.rope.pairs = addr(4), addr(5), T, dr // 2
+    a.dq_pre, a.dx, a.dw, a.dw_dtype = addr(6), addr(7), addr(8), bd.DTYPE_BF16
+    a.use_bias, a.db = 1, addr(9)
+    a.workspace, a.workspace_bytes = addr(10), 1 << 30
+    for k, v in over.items():
+        obj = a
+        *path, last = k.split("__")
+        for p in path:
+            obj = getattr(obj, p)
+        setattr(obj, last, v)
+    return a
+
+
+def test_bwd_workspace_size(L):
+    a = bwd_args()
+    need = L.mla_qup_bwd_workspace_size(ctypes.byref(a))
+    assert need > 0 and need % 256 == 0
+    b = bwd_args(use_bias=0, dx=0)
+    assert L.mla_qup_bwd_workspace_size(ctypes.byref(b)) == 0
+    assert L.mla_qup_bwd_workspace_size(ctypes.byref(bwd_args(K=10))) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(db=0), bd.MLA_EINVAL),                 # use_bias without a db buffer
+    (dict(use_bias=2), bd.MLA_EINVAL),
+    (dict(dq_pre=0), bd.MLA_EINVAL),
+    (dict(dw_dtype=bd.DTYPE_MXFP8), bd.MLA_EINVAL),
+    (dict(workspace=0), bd.MLA_EWORKSPACE),
+    (dict(workspace_bytes=1024), bd.MLA_EWORKSPACE),
+    (dict(workspace=addr(10, 16)), bd.MLA_EINVAL),
+    (dict(rope__pairs=16), bd.MLA_EROPE_TABLE),
+    (dict(dx=addr(1, 512)), bd.MLA_EALIAS),      # dx inside dq
+    (dict(dw=addr(6, 1024)), bd.MLA_EALIAS),     # dw inside dq_pre
+    (dict(db=addr(10, 4096)), bd.MLA_EALIAS),    # db inside the workspace
+])
+def test_bwd_validation(L, over, code):
+    assert L.mla_qup_bwd(ctypes.byref(bwd_args(**over)), None) == code
+
+
+def test_rope_and_quantize_validation(L):
+    y = bd.mla_yarn(40.0, 4096, 32.0, 1.0, 1.0)
+    assert L.rope_cache_build(None, addr(2), 16, 64, 1e4, None, None) == bd.MLA_EINVAL
+    assert L.rope_cache_build(addr(1), addr(2), 16, 63, 1e4, None, None) == bd.MLA_EINVAL
+    assert L.rope_cache_build(addr(1), addr(2), 16, 64, 1.0, None, None) == bd.MLA_EINVAL
+    bad = bd.mla_yarn(0.0, 4096, 32.0, 1.0, 1.0)
+    assert L.rope_cache_build(addr(1), addr(2), 16, 64, 1e4, ctypes.byref(bad), None) == bd.MLA_EINVAL
+    assert L.rope_cache_build(addr(1), addr(1, 64), 16, 64, 1e4, ctypes.byref(y), None) == bd.MLA_EALIAS
+    assert L.mxfp8_quantize(addr(1), bd.DTYPE_MXFP8, 4, 64, 64, addr(2), addr(3), None) == bd.MLA_EINVAL
+    assert L.mxfp8_quantize(addr(1), bd.DTYPE_BF16, 4, 48, 48, addr(2), addr(3), None) == bd.MLA_EINVAL
+    assert L.mxfp8_quantize(addr(1), bd.DTYPE_BF16, 4, 64, 60, addr(2), addr(3), None) == bd.MLA_EINVAL
+    assert L.mxfp8_quantize(addr(1), bd.DTYPE_BF16, 4, 64, 64, addr(1, 64), addr(3), None) == bd.MLA_EALIAS
+    assert L.mxfp8_quantize(addr(1), bd.DTYPE_BF16, 0, 64, 64, 0, 0, None) == bd.MLA_OK
+
+
+def test_binding_raises_without_library(monkeypatch):
+    monkeypatch.setattr(bd, "_lib", None)
+    monkeypatch.setattr(bd, "LIB_PATH", "/nonexistent/libmlaqup.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        bd.lib()

@@ -1,0 +1,458 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU.
+
+Small cases compare every output element; the five named workloads run at
+their full sizes in the same launch configuration the benchmark times, and
+the oracle checks sampled token rows (plus full-size properties: input bytes
+unchanged, run-to-run bit identity, every output element written).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_up_projection_amd as m
+import oracle as o
+from mla_up_projection_amd import synthetic as syn
+from parity import bits16, check_bf16, check_mx, frob_rel, fwd_reference_rows, u8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _dev(t):
+    return t.to(DEV)
+
+
+def rope_tables(rows, d_rope, base=1e4, yarn=None):
+    """GPU table from rope_cache_build, oracle table from the oracle."""
+    pairs = max(d_rope // 2, 1)
+    cos = torch.empty(rows, pairs, dtype=torch.float32, device=DEV)
+    sin = torch.empty_like(cos)
+    if d_rope:
+        m.rope_cache_build(cos, sin, d_rope, base, yarn)
+    oy = o.Yarn(*yarn) if yarn is not None else None
+    oc, os_ = o.rope_table(rows, d_rope, base, oy)
+    return cos, sin, oc, os_
+
+
+def run_fwd(x, w, *, H, dn, dr, out_mx, fmt=m.FMT_BSHD, B=1, S=None, cu=None, max_seqlen=None,
+            yarn=None, bias=None, x_scales=None, w_scales=None, rows=None):
+    """Run the GPU forward; returns (out, scales, oracle tables). Outputs are
+    prefilled with a NaN pattern so unwritten elements are visible."""
+    T = x.shape[0]
+    D = dn + dr
+    if S is None:
+        S = T // B
+    max_pos = max_seqlen if fmt == m.FMT_THD else S
+    cos, sin, oc, os_ = rope_tables(rows or max_pos, dr, yarn=yarn)
+    shape = o.out_shape(fmt, T, H, D, B, S)
+    if out_mx:
+        out = torch.full(shape, 0x7F, dtype=torch.uint8, device=DEV)
+        sc = torch.full(shape[:3] + (D // 32,), 0xFF, dtype=torch.uint8, device=DEV)
+    else:
+        out = torch.full(shape, -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)  # NaN
+        sc = None
+    m.mla_qup_fwd(x, w, out, H=H, d_nope=dn, d_rope=dr, cos=cos if dr else None,
+                  sin=sin if dr else None, x_scales=x_scales, w_scales=w_scales, bias=bias,
+                  out_scales=sc, fmt=fmt, B=B, S=S, cu_seqlens=cu, max_seqlen=max_seqlen)
+    torch.cuda.synchronize()
+    return out, sc, oc, os_
+
+
+# ------------------------------------------------------------ rope table ----
+@pytest.mark.parametrize("rows,d,yarn", [(64, 16, None), (4096, 64, None),
+                                         (4096, 64, (40.0, 4096, 32.0, 1.0, 1.0)),
+                                         (300, 64, (40.0, 4096, 32.0, 1.0, 1.3688))])
+def test_rope_cache_matches_oracle(rows, d, yarn):
+    cos, sin, oc, os_ = rope_tables(rows, d, yarn=yarn)
+    for g, r in ((cos.cpu().numpy(), oc), (sin.cpu().numpy(), os_)):
+        ulp = np.abs(g.view(np.int32).astype(np.int64) - r.view(np.int32).astype(np.int64))
+        # both round a float64 cos/sin to float32; libm and device math may
+        # differ in the last double bit, which moves a float32 rounding at most
+        # one step, and rarely
+        assert ulp.max() <= 1 and (ulp > 0).mean() <= 1e-3
+
+
+# --------------------------------------------------------- mxfp8_quantize ----
+def test_mxfp8_quantize_bf16_exhaustive_bitexact():
+    """All 65536 bf16 patterns, in 2048 blocks of 32 (blocks holding NaN or Inf
+    become 0xFF / 0x7F), plus a shuffled copy for mixed-magnitude blocks."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    perm = np.random.default_rng(5).permutation(65536)
+    allb = np.concatenate([bits, bits[perm]]).reshape(-1, 256)
+    x = torch.from_numpy(allb.view(np.int16)).view(torch.bfloat16)
+    xd = _dev(x)
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(x.shape[0], x.shape[1] // 32, dtype=torch.uint8, device=DEV)
+    m.mxfp8_quantize(xd, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = o.mxfp8_quantize_blocks(o.to_f64(x).astype(np.float32))
+    assert np.array_equal(u8(scales), rs)
+    assert np.array_equal(u8(codes), rc)
+
+
+def test_mxfp8_quantize_fp32_special_values_and_stride():
+    rng = np.random.default_rng(3)
+    v = (rng.standard_normal((96, 192)) * 0.784).astype(np.float32)
+    v[1, :32] = 0.0
+    v[2, :32] = -0.0
+    v[3, :32] = np.float32(1e-40) * rng.standard_normal(32).astype(np.float32)  # subnormals
+    v[4, 32:64] = np.float32(3e38)
+    v[5, 5] = np.nan
+    v[6, 70] = -np.inf
+    # exact E4M3 ties after scaling by 2^-E (amax 448 gives E = 0)
+    v[7, :6] = [448.0, 17.0, 19.0, 0.0029296875, 0.0009765625, -0.0048828125]
+    v[8, :32] = np.float32(2.0 ** -130)   # amax float32-subnormal: E clamps to -127
+    base = np.zeros((96, 256), np.float32)
+    base[:, :192] = v
+    xd = _dev(torch.from_numpy(base))[:, :192]     # row stride 256 > cols
+    codes = torch.empty(96, 192, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(96, 6, dtype=torch.uint8, device=DEV)
+    m.mxfp8_quantize(xd, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = o.mxfp8_quantize_blocks(v)
+    assert np.array_equal(u8(scales), rs)
+    assert np.array_equal(u8(codes), rc)
+
+
+# ------------------------------------------------------------- forward ------
+def full_compare_fwd(x, w, *, H, dn, dr, fmt=m.FMT_BSHD, B=1, S=None, cu=None, max_seqlen=None,
+                     yarn=None, bias=None, mx_in=False):
+    T, K = x.shape
+    S = S if S is not None else T // B
+    xs = ws = xq = wq = None
+    xd, wd = _dev(x), _dev(w)
+    if mx_in:
+        xq = torch.empty(T, K, dtype=torch.uint8, device=DEV)
+        xs = torch.empty(T, K // 32, dtype=torch.uint8, device=DEV)
+        wq = torch.empty(w.shape, dtype=torch.uint8, device=DEV)
+        ws = torch.empty(w.shape[0], K // 32, dtype=torch.uint8, device=DEV)
+        m.mxfp8_quantize(xd, xq, xs)
+        m.mxfp8_quantize(wd, wq, ws)
+        xd, wd = xq, wq
+    cud = _dev(cu) if cu is not None else None
+    bd_ = _dev(bias) if bias is not None else None
+    res = {}
+    for out_mx in (False, True):
+        out, sc, oc, os_ = run_fwd(xd, wd, H=H, dn=dn, dr=dr, out_mx=out_mx, fmt=fmt, B=B, S=S,
+                                   cu=cud, max_seqlen=max_seqlen, yarn=yarn, bias=bd_,
+                                   x_scales=xs, w_scales=ws)
+        # oracle: quantizes X and W itself on the MXFP8 path
+        if mx_in:
+            oxq, oxs = o.mxfp8_quantize_blocks(o.to_f64(x).astype(np.float32))
+            owq, ows = o.mxfp8_quantize_blocks(o.to_f64(w).astype(np.float32))
+            assert np.array_equal(u8(xq), oxq) and np.array_equal(u8(xs), oxs)
+            ox, ow = oxq, owq
+        else:
+            ox, ow, oxs, ows = x, w, None, None
+        pos, bb, ss = o.token_coords(fmt, T, B, S, cu.numpy() if cu is not None else None)
+        rows = np.arange(T)
+        q64, bound = fwd_reference_rows(ox, ow, bias, rows, H=H, d_nope=dn, d_rope=dr, cos=oc,
+                                        sin=os_, pos=pos, x_scales=oxs if mx_in else None,
+                                        w_scales=ows if mx_in else None)
+        g = out.cpu()
+        g_rows = g[bb, :, ss, :]                  # [T, H, D] token-major
+        if out_mx:
+            g_sc = sc.cpu()[bb, :, ss, :]
+            res["mx"] = check_mx(g_rows.numpy(), g_sc.numpy(), q64, bound)
+            print("\nmx", res["mx"], flush=True)
+            # every element written: BHSD has no slot outside the token rows
+            assert g.numel() == g_rows.numel() and sc.numel() == g_sc.numel()
+        else:
+            r_bits = o.f32_to_bf16_bits(q64.astype(np.float32))
+            res["bf16"] = check_bf16(bits16(g_rows), r_bits)
+    return res
+
+
+def test_fwd_tiny_workload():
+    w = syn.workload("tiny")
+    full_compare_fwd(w.x(), w.w(), H=w.H, dn=w.d_nope, dr=w.d_rope, B=1, S=w.T)
+
+
+@pytest.mark.parametrize("fmt,B,S", [(m.FMT_BSHD, 1, 333), (m.FMT_SBHD, 3, 111), (m.FMT_BSHD, 3, 111)])
+def test_fwd_ragged_multi_tile(fmt, B, S):
+    """T = 333 (two token tiles, ragged), N = 960 (five N tiles), K = 256, bias."""
+    T, K, H = B * S, 256, 5
+    x = syn.normal_bf16((T, K), 1.0, 10)
+    w = syn.normal_bf16((H * 192, K), 0.05, 11)
+    bias = syn.normal_bf16((H * 192,), 0.3, 12)
+    full_compare_fwd(x, w, H=H, dn=128, dr=64, fmt=fmt, B=B, S=S, bias=bias)
+
+
+@pytest.mark.parametrize("dn,dr,H", [(32, 0, 3), (0, 64, 2), (16, 16, 7)])
+def test_fwd_head_layouts(dn, dr, H):
+    T, K = 200, 96
+    x = syn.normal_bf16((T, K), 1.0, 20)
+    w = syn.normal_bf16((H * (dn + dr), K), 0.1, 21)
+    full_compare_fwd(x, w, H=H, dn=dn, dr=dr, B=1, S=T)
+
+
+def test_fwd_thd_yarn_small():
+    lengths = [100, 37, 200, 1]
+    cu = syn.cu_seqlens_of(lengths)
+    T, K, H = sum(lengths), 128, 3
+    x = syn.normal_bf16((T, K), 1.0, 30)
+    w = syn.normal_bf16((H * 192, K), 0.05, 31)
+    full_compare_fwd(x, w, H=H, dn=128, dr=64, fmt=m.FMT_THD, cu=cu, max_seqlen=max(lengths),
+                     yarn=(40.0, 4096, 32.0, 1.0, 1.0))
+
+
+def test_fwd_mxfp8_projection_small():
+    T, K, H = 300, 256, 3
+    x = syn.normal_bf16((T, K), 1.0, 40)
+    w = syn.normal_bf16((H * 192, K), 0.02, 41)
+    full_compare_fwd(x, w, H=H, dn=128, dr=64, B=1, S=T, mx_in=True)
+
+
+@pytest.mark.parametrize("fp8_mfma", [False, True])
+def test_fwd_mxfp8_operands_narrow_codes_random_scales(fp8_mfma):
+    """MXFP8 X and W given directly: every code has exponent field 7 (values
+    +-1..1.875), scales vary per 32-block. Products then never differ by more
+    than 2^4, so the result is exact up to fp32 summation: this isolates the
+    operand/scale layout of the scaled MFMA from its dot-product precision."""
+    T, K, H, D = 256, 512, 2, 192
+    rng = np.random.default_rng(80)
+    def codes(shape):
+        return ((rng.integers(0, 2, shape) << 7) | (7 << 3) | rng.integers(0, 8, shape)).astype(np.uint8)
+    xc, wc = codes((T, K)), codes((H * D, K))
+    xs = rng.integers(118, 136, (T, K // 32)).astype(np.uint8)
+    ws = rng.integers(112, 130, (H * D, K // 32)).astype(np.uint8)
+    cos, sin, oc, os_ = rope_tables(T, 64)
+    out = torch.full((1, H, T, D), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    m.mla_qup_fwd(_dev(torch.from_numpy(xc)), _dev(torch.from_numpy(wc)), out, H=H, d_nope=128,
+                  d_rope=64, cos=cos, sin=sin, x_scales=_dev(torch.from_numpy(xs)),
+                  w_scales=_dev(torch.from_numpy(ws)), B=1, S=T, fp8_mfma=fp8_mfma)
+    torch.cuda.synchronize()
+    pos = np.arange(T)
+    q64, bound = fwd_reference_rows(xc, wc, None, pos, H=H, d_nope=128, d_rope=64, cos=oc, sin=os_,
+                                    pos=pos, x_scales=xs, w_scales=ws)
+    g = o.bf16_bits_to_f64(bits16(out[0].transpose(0, 1)))
+    r = o.bf16_bits_to_f64(o.f32_to_bf16_bits(q64.astype(np.float32)))
+    # bf16 rounding of values that agree to fp32 accuracy: at most one bf16 step apart
+    assert (np.abs(g - r) <= np.abs(r) * 2.0 ** -7 + 1e-30).all()
+
+
+def test_fwd_fp8_mfma_mode_accuracy():
+    """Opt-in scaled-FP8-MFMA mode on MX-quantized DeepSeek-V3-like operands.
+    Its dot products are summed in the instruction's narrower fixed-point
+    window, so the bar is a relative Frobenius error of 1e-2 on the bf16
+    output (the deviation is printed) rather than the MXFP8 code bar."""
+    T, K, H = 512, 1536, 4
+    x = syn.normal_bf16((T, K), 1.0, 0)
+    w = syn.normal_bf16((H * 192, K), 0.02, 1)
+    xq = torch.empty(T, K, dtype=torch.uint8, device=DEV)
+    xs = torch.empty(T, K // 32, dtype=torch.uint8, device=DEV)
+    wq = torch.empty(w.shape, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(w.shape[0], K // 32, dtype=torch.uint8, device=DEV)
+    m.mxfp8_quantize(_dev(x), xq, xs)
+    m.mxfp8_quantize(_dev(w), wq, ws)
+    cos, sin, oc, os_ = rope_tables(T, 64)
+    out = torch.empty(1, H, T, 192, dtype=torch.bfloat16, device=DEV)
+    m.mla_qup_fwd(xq, wq, out, H=H, d_nope=128, d_rope=64, cos=cos, sin=sin, x_scales=xs,
+                  w_scales=ws, B=1, S=T, fp8_mfma=True)
+    torch.cuda.synchronize()
+    pos = np.arange(T)
+    q64, _ = fwd_reference_rows(u8(xq), u8(wq), None, pos, H=H, d_nope=128, d_rope=64, cos=oc,
+                                sin=os_, pos=pos, x_scales=u8(xs), w_scales=u8(ws))
+    g = o.bf16_bits_to_f64(bits16(out[0].transpose(0, 1)))
+    rms = np.sqrt((q64 ** 2).mean())
+    rel = frob_rel(g, q64)
+    print(f"\nfp8-mfma mode: rel Frobenius {rel:.3e}, max abs err / RMS {np.abs(g - q64).max() / rms:.3e}")
+    assert rel <= 1e-2
+
+
+def test_fwd_zero_tokens_enqueues_nothing():
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros(64, 64, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty(1, 2, 0, 32, dtype=torch.bfloat16, device=DEV)
+    cu = torch.zeros(2, dtype=torch.int32, device=DEV)
+    cos = torch.ones(4, 8, device=DEV)
+    m.mla_qup_fwd(x, w, out, H=2, d_nope=16, d_rope=16, cos=cos, sin=cos, fmt=m.FMT_THD,
+                  cu_seqlens=cu, max_seqlen=1)
+    torch.cuda.synchronize()
+
+
+def test_fwd_position_beyond_table_is_nan_not_a_read():
+    """A THD sequence longer than the max_seqlen the caller promised: the
+    kernel's own bound check turns the rotated elements of positions past the
+    table into NaN (MXFP8: scale 0xFF) instead of reading past it."""
+    lengths = [40, 30]
+    cu = _dev(syn.cu_seqlens_of(lengths))
+    T, K, H = 70, 64, 1
+    x = _dev(syn.normal_bf16((T, K), 1.0, 50))
+    w = _dev(syn.normal_bf16((64, K), 0.1, 51))
+    cos = torch.empty(32, 16, device=DEV)
+    sin = torch.empty_like(cos)
+    m.rope_cache_build(cos, sin, 32, 1e4)
+    out = torch.empty(1, 2, T, 32, dtype=torch.uint8, device=DEV)   # H=2 heads of 32
+    sc = torch.empty(1, 2, T, 1, dtype=torch.uint8, device=DEV)
+    m.mla_qup_fwd(x, w, out, H=2, d_nope=0, d_rope=32, cos=cos, sin=sin, out_scales=sc,
+                  fmt=m.FMT_THD, cu_seqlens=cu, max_seqlen=32)
+    torch.cuda.synchronize()
+    s = sc.cpu()[0, :, :, 0]
+    pos = np.array(list(range(40)) + list(range(30)))
+    assert (s[:, pos >= 32] == 0xFF).all() and (s[:, pos < 32] != 0xFF).all()
+
+
+# ------------------------------------------------------------ backward ------
+def run_bwd(dq, x, w, *, H, dn, dr, fmt=m.FMT_BSHD, B=1, S=None, cu=None, max_seqlen=None,
+            use_bias=True, dw_fp32=False, yarn=None):
+    T, K = x.shape
+    N = H * (dn + dr)
+    S = S if S is not None else T // B
+    max_pos = max_seqlen if fmt == m.FMT_THD else S
+    cos, sin, oc, os_ = rope_tables(max_pos, dr, yarn=yarn)
+    dqd, xd, wd = _dev(dq), _dev(x), _dev(w)
+    dq_pre = torch.empty(T, N, dtype=torch.bfloat16, device=DEV)
+    dx = torch.empty(T, K, dtype=torch.bfloat16, device=DEV)
+    dw = torch.empty(N, K, dtype=torch.float32 if dw_fp32 else torch.bfloat16, device=DEV)
+    db = torch.empty(N, dtype=torch.bfloat16, device=DEV) if use_bias else None
+    kw = dict(H=H, d_nope=dn, d_rope=dr, cos=cos if dr else None, sin=sin if dr else None,
+              dx=dx, dw=dw, db=db, use_bias=use_bias, fmt=fmt, B=B, S=S,
+              cu_seqlens=_dev(cu) if cu is not None else None, max_seqlen=max_seqlen)
+    nbytes = m.mla_qup_bwd_workspace_size(dqd, xd, wd, dq_pre, **kw)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    m.mla_qup_bwd(dqd, xd, wd, dq_pre, workspace=ws if nbytes else None, **kw)
+    torch.cuda.synchronize()
+    return dict(dq_pre=dq_pre, dx=dx, dw=dw, db=db, oc=oc, os=os_)
+
+
+def test_bwd_small_against_oracle():
+    T, K, H = 333, 256, 5
+    x = syn.normal_bf16((T, K), 1.0, 60)
+    w = syn.normal_bf16((H * 192, K), 0.02, 61)
+    dq = syn.normal_bf16((T, H, 192), 1e-3, 62)
+    for dw_fp32 in (False, True):
+        g = run_bwd(dq, x, w, H=H, dn=128, dr=64, S=T, dw_fp32=dw_fp32)
+        r = o.qup_backward(dq, x, w, H=H, d_nope=128, d_rope=64, cos=g["oc"], sin=g["os"], S=T)
+        check_bf16(bits16(g["dq_pre"]), o.f32_to_bf16_bits(r.dq_pre.astype(np.float32)), "dq_pre")
+        assert frob_rel(o.to_f64(g["dx"].cpu()), r.dx) <= 1e-2
+        assert frob_rel(o.to_f64(g["dw"].cpu()), r.dw) <= 1e-2
+        assert frob_rel(o.to_f64(g["db"].cpu()), r.db) <= 1e-2
+
+
+def test_bwd_thd_yarn_no_bias():
+    lengths = [64, 129, 7]
+    cu = syn.cu_seqlens_of(lengths)
+    T, K, H = sum(lengths), 192, 2
+    x = syn.normal_bf16((T, K), 1.0, 70)
+    w = syn.normal_bf16((H * 192, K), 0.02, 71)
+    dq = syn.normal_bf16((T, H, 192), 1e-3, 72)
+    yarn = (40.0, 4096, 32.0, 1.0, 1.0)
+    g = run_bwd(dq, x, w, H=H, dn=128, dr=64, fmt=m.FMT_THD, cu=cu, max_seqlen=129,
+                use_bias=False, yarn=yarn)
+    r = o.qup_backward(dq, x, w, H=H, d_nope=128, d_rope=64, cos=g["oc"], sin=g["os"],
+                       fmt=o.FMT_THD, cu_seqlens=cu.numpy())
+    check_bf16(bits16(g["dq_pre"]), o.f32_to_bf16_bits(r.dq_pre.astype(np.float32)), "dq_pre")
+    assert frob_rel(o.to_f64(g["dx"].cpu()), r.dx) <= 1e-2
+    assert frob_rel(o.to_f64(g["dw"].cpu()), r.dw) <= 1e-2
+
+
+def test_bwd_zero_tokens_zeroes_dw_db():
+    K, H = 64, 2
+    x = torch.empty(0, K, dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(64, K, dtype=torch.bfloat16, device=DEV)
+    dq = torch.empty(0, H, 32, dtype=torch.bfloat16, device=DEV)
+    dq_pre = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    dw = torch.full((64, K), 7.0, dtype=torch.bfloat16, device=DEV)
+    db = torch.full((64,), 7.0, dtype=torch.bfloat16, device=DEV)
+    cos = torch.ones(4, 8, device=DEV)
+    cu = torch.zeros(2, dtype=torch.int32, device=DEV)
+    m.mla_qup_bwd(dq, x, w, dq_pre, H=H, d_nope=16, d_rope=16, cos=cos, sin=cos, dw=dw, db=db,
+                  use_bias=True, fmt=m.FMT_THD, cu_seqlens=cu, max_seqlen=1)
+    torch.cuda.synchronize()
+    assert (dw.float() == 0).all() and (db.float() == 0).all()
+
+
+# ------------------------------------------------ full-size named workloads --
+SAMPLE = 96
+
+
+def sample_rows(T, seed=123):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, T // 2, T - 2, T - 1], rng.integers(0, T, SAMPLE)]))
+    return rows
+
+
+def _hash(t):
+    return hash(t.detach().cpu().contiguous().view(torch.uint8).numpy().tobytes())
+
+
+@pytest.mark.parametrize("name", ["dsv3_fwd_bf16w", "dsv3_fwd_mxfp8w", "thd_yarn_fwd"])
+def test_fwd_full_size_sampled(name):
+    wl = syn.workload(name)
+    x, w = wl.x(), wl.w()
+    T, K = x.shape
+    xd, wd = _dev(x), _dev(w)
+    cu = wl.cu_seqlens()
+    cud = _dev(cu) if cu is not None else None
+    yarn = wl.yarn
+    max_pos = wl.max_pos
+    cos, sin, oc, os_ = rope_tables(max_pos, wl.d_rope, yarn=yarn)
+    hx, hw, hc = _hash(xd), _hash(wd), _hash(cos)
+    xs = ws = None
+    if wl.mx_weight:
+        xq = torch.empty(T, K, dtype=torch.uint8, device=DEV)
+        xs = torch.empty(T, K // 32, dtype=torch.uint8, device=DEV)
+        wq = torch.empty(w.shape, dtype=torch.uint8, device=DEV)
+        ws = torch.empty(w.shape[0], K // 32, dtype=torch.uint8, device=DEV)
+        m.mxfp8_quantize(xd, xq, xs)
+        m.mxfp8_quantize(wd, wq, ws)
+        torch.cuda.synchronize()
+        oxq, oxs = o.mxfp8_quantize_blocks(o.to_f64(x).astype(np.float32))
+        owq, ows = o.mxfp8_quantize_blocks(o.to_f64(w).astype(np.float32))
+        assert np.array_equal(u8(xs), oxs) and np.array_equal(u8(ws), ows)
+        assert np.array_equal(u8(xq), oxq) and np.array_equal(u8(wq), owq)
+        xin, win = xq, wq
+    else:
+        xin, win = xd, wd
+    shape = o.out_shape(wl.fmt, T, wl.H, wl.D, wl.B, wl.S)
+    outs = []
+    for rep in range(2):
+        out = torch.full(shape, 0x7F, dtype=torch.uint8, device=DEV)
+        sc = torch.full(shape[:3] + (wl.D // 32,), 0xFF, dtype=torch.uint8, device=DEV)
+        m.mla_qup_fwd(xin, win, out, H=wl.H, d_nope=wl.d_nope, d_rope=wl.d_rope, cos=cos, sin=sin,
+                      x_scales=xs, w_scales=ws, out_scales=sc, fmt=wl.fmt, B=wl.B, S=wl.S,
+                      cu_seqlens=cud, max_seqlen=max_pos)
+        torch.cuda.synchronize()
+        outs.append((out, sc))
+    # determinism and completeness (finite inputs never give 0xFF scales)
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert not (outs[0][1] == 0xFF).any()
+    # inputs untouched, byte for byte
+    assert _hash(xd) == hx and _hash(wd) == hw and _hash(cos) == hc
+    out, sc = outs[0]
+    rows = sample_rows(T)
+    pos, bb, ss = o.token_coords(wl.fmt, T, wl.B, wl.S, cu.numpy() if cu is not None else None)
+    if wl.mx_weight:
+        q64, bound = fwd_reference_rows(oxq, owq, None, rows, H=wl.H, d_nope=wl.d_nope,
+                                        d_rope=wl.d_rope, cos=oc, sin=os_, pos=pos, x_scales=oxs,
+                                        w_scales=ows)
+    else:
+        q64, bound = fwd_reference_rows(x, w, None, rows, H=wl.H, d_nope=wl.d_nope,
+                                        d_rope=wl.d_rope, cos=oc, sin=os_, pos=pos)
+    bi, si = torch.from_numpy(bb[rows]).to(DEV), torch.from_numpy(ss[rows]).to(DEV)
+    g = out[bi, :, si, :].cpu().numpy()
+    gs = sc[bi, :, si, :].cpu().numpy()
+    stats = check_mx(g, gs, q64, bound, name)
+    print(f"\n{name}: {stats}", flush=True)
+
+
+def test_bwd_full_size_sampled():
+    wl = syn.workload("dsv3_bwd")
+    x, w, dq = wl.x(), wl.w(), wl.dq()
+    T, K, N = wl.T, wl.K, wl.N
+    g = run_bwd(dq, x, w, H=wl.H, dn=wl.d_nope, dr=wl.d_rope, S=wl.S, use_bias=True)
+    pos, _, _ = o.token_coords(o.FMT_BSHD, T, 1, T)
+    dq64 = o.to_f64(dq)
+    dq_pre = o.rope_rotate(dq64, pos, g["oc"], g["os"], wl.d_nope, wl.d_rope, inverse=True).reshape(T, N)
+    rows = sample_rows(T)
+    check_bf16(bits16(g["dq_pre"][torch.from_numpy(rows).to(DEV)]),
+               o.f32_to_bf16_bits(dq_pre[rows].astype(np.float32)), "dq_pre")
+    wf, xf = o.to_f64(w), o.to_f64(x)
+    dx_ref = dq_pre[rows] @ wf
+    assert frob_rel(o.to_f64(g["dx"][torch.from_numpy(rows).to(DEV)].cpu()), dx_ref) <= 1e-2
+    nrows = sample_rows(N, seed=7)
+    dw_ref = dq_pre[:, nrows].T @ xf
+    assert frob_rel(o.to_f64(g["dw"][torch.from_numpy(nrows).to(DEV)].cpu()), dw_ref) <= 1e-2
+    assert frob_rel(o.to_f64(g["db"].cpu()), dq_pre.sum(0)) <= 1e-2
