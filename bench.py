@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MLA query up-projection on one MI355X.
+
+One step = the whole hot path over one batch at DeepSeek-V3 shape
+(T=4096 tokens, q_lora_rank K=1536, 128 heads of 128+64):
+  rope_cache_build (4096 x 32 table)
+  -> mla_qup_fwd: GEMM + RoPE + MXFP8 quantization, BHSD output, BF16 weight
+  -> mla_qup_bwd: inverse RoPE, db, dX, dW (bias gradient on).
+Throughput is the step's GEMM FLOPs (2TNK forward + 4TNK backward) over the
+step time, in TFLOP/s. Inputs are seeded synthetic tensors, resident in HBM
+before the timed region. The MXFP8-projection path (quantize + forward at
+T=8192) and the MXFP8 quantizer are timed in separate legs after the timed
+region. The CPU oracle is timed on a bounded token sample of the same step.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+METRIC = "fused Q-up-proj fwd/bwd TFLOP/s and % MFMA peak at DeepSeek-V3 shape, 1 GPU"
+FWD_KERNEL_SRC = os.path.join(ROOT, "mla_up_projection_amd", "csrc", "qup_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qup_fwd_bf16_dsv3_traffic.md")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--legs-reps", type=int, default=20)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def fwd_traffic(n_launch_bytes_alg: float):
+    """HBM bytes per launch of the fused forward from the committed counter
+    summary, or None if it is absent or was taken on another kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
+    if not m_bytes or not m_src:
+        return None
+    cur = hashlib.sha256(open(FWD_KERNEL_SRC, "rb").read()).hexdigest()
+    if cur != m_src.group(1):
+        return None
+    return float(m_bytes.group(1))
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the operation runs on a single GPU; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mla_up_projection_amd as m
+    from mla_up_projection_amd import synthetic as syn
+
+    if not os.path.exists(m.LIB_PATH):
+        from mla_up_projection_amd import build
+        build.build()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    wf = syn.workload("dsv3_fwd_bf16w")
+    wb = syn.workload("dsv3_bwd")
+    T, K, H, dn, dr = wf.T, wf.K, wf.H, wf.d_nope, wf.d_rope
+    D, N = wf.D, wf.N
+
+    # ---- inputs resident in HBM ----
+    x = wf.x().to(dev)
+    w = wf.w().to(dev)
+    dq = wb.dq().to(dev)
+    cos = torch.empty(wf.S, dr // 2, dtype=torch.float32, device=dev)
+    sin = torch.empty_like(cos)
+    out = torch.empty(1, H, T, D, dtype=torch.uint8, device=dev)
+    out_sc = torch.empty(1, H, T, D // 32, dtype=torch.uint8, device=dev)
+    dq_pre = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    dx = torch.empty(T, K, dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+    db = torch.empty(N, dtype=torch.bfloat16, device=dev)
+    bkw = dict(H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin, dx=dx, dw=dw, db=db, use_bias=True,
+               B=1, S=T)
+    ws_bytes = m.mla_qup_bwd_workspace_size(dq, x, w, dq_pre, **bkw)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        m.rope_cache_build(cos, sin, dr, 10000.0)
+        if ev is not None:
+            ev[0].record(stream)
+        m.mla_qup_fwd(x, w, out, H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin, out_scales=out_sc,
+                      B=1, S=T)
+        if ev is not None:
+            ev[1].record(stream)
+        m.mla_qup_bwd(dq, x, w, dq_pre, workspace=ws, **bkw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    flops_fwd = 2.0 * T * N * K
+    flops_bwd = 4.0 * T * N * K
+    tflops = (flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12
+    fwd_tflops = flops_fwd / (fwd_ms * 1e-3) / 1e12
+    bwd_ms = ms_step - fwd_ms
+
+    # ---- separate legs (after the timed region) ----
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    parts = {"qup_fwd_bf16_dsv3": {"ms": fwd_ms, "tflops": fwd_tflops,
+                                   "pct_bf16_peak": 100 * fwd_tflops / BF16_PEAK_TFLOPS},
+             "qup_bwd_dsv3": {"ms": bwd_ms, "tflops": flops_bwd / (bwd_ms * 1e-3) / 1e12}}
+    R = args.legs_reps
+    # MXFP8 projection path, T = 8192 (2 x 4096)
+    w2 = syn.workload("dsv3_fwd_mxfp8w")
+    x2 = w2.x().to(dev)
+    xq = torch.empty(w2.T, K, dtype=torch.uint8, device=dev)
+    xs = torch.empty(w2.T, K // 32, dtype=torch.uint8, device=dev)
+    wq = torch.empty(N, K, dtype=torch.uint8, device=dev)
+    wsc = torch.empty(N, K // 32, dtype=torch.uint8, device=dev)
+    m.mxfp8_quantize(w, wq, wsc)
+    out2 = torch.empty(w2.B, H, w2.S, D, dtype=torch.uint8, device=dev)
+    out2_sc = torch.empty(w2.B, H, w2.S, D // 32, dtype=torch.uint8, device=dev)
+    q_ms = timed(lambda: m.mxfp8_quantize(x2, xq, xs), R)
+    q_bytes = w2.T * K * (2 + 1 + 1 / 32)
+    parts["mxfp8_quantize_x_8192x1536"] = {"ms": q_ms, "gbs": q_bytes / (q_ms * 1e-3) / 1e9,
+                                           "pct_hbm_peak": 100 * q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    f2 = 2.0 * w2.T * N * K
+    for mode, fp8 in (("exact_bf16_mfma", False), ("fp8_mfma", True)):
+        ms2 = timed(lambda: m.mla_qup_fwd(xq, wq, out2, H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin,
+                                          x_scales=xs, w_scales=wsc, out_scales=out2_sc, B=w2.B,
+                                          S=w2.S, fp8_mfma=fp8), R)
+        tf = f2 / (ms2 * 1e-3) / 1e12
+        parts[f"qup_fwd_mxfp8w_dsv3_{mode}"] = {
+            "ms": ms2, "tflops": tf, "pct_bf16_peak": 100 * tf / BF16_PEAK_TFLOPS,
+            "pct_fp8_peak": 100 * tf / FP8_PEAK_TFLOPS}
+    del x2, xq, wq, out2
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        parts["calib_copy_bytes"] = n
+
+    traffic = fwd_traffic(flops_fwd)
+    roofline = {"bound": "mfma", "kernel": "qup_fwd_kernel<bf16> (fused GEMM+RoPE+MXFP8)",
+                "achieved": fwd_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": fwd_tflops / BF16_PEAK_TFLOPS, "traffic": traffic}
+
+    # ---- CPU oracle on a bounded sample ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_sample_tokens, x, w, dq, dn, dr, H)
+
+    line = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "pct_bf16_peak": 100 * tflops / BF16_PEAK_TFLOPS,
+        "config": {"workload": "DeepSeek-V3 MLA q up-projection step: rope table + fused forward "
+                               "(BF16 weight, MXFP8 BHSD out) + backward (inverse RoPE, dX, dW, db)",
+                   "T": T, "K": K, "H": H, "d_nope": dn, "d_rope": dr, "seq": "1x4096",
+                   "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "parts": parts,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(ts, x, w, dq, dn, dr, H):
+    """The oracle, as it stands, on the first `ts` tokens of the step's
+    workload: forward (GEMM, RoPE, MXFP8) and backward for those tokens."""
+    import numpy as np
+    import oracle as o
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    xs, wc, dqs = x[:ts].cpu(), w.cpu(), dq[:ts].cpu()
+    cos, sin = o.rope_table(4096, dr, 1e4)
+    K = xs.shape[1]
+    N = wc.shape[0]
+    t0 = time.perf_counter()
+    o.qup_forward(xs, wc, H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin, B=1, S=ts)
+    o.qup_backward(dqs, xs, wc, H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin, B=1, S=ts)
+    dt = time.perf_counter() - t0
+    flops = 6.0 * ts * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"first {ts} of 4096 tokens of the step (forward + backward, all 128 heads), "
+                      "float64 numpy"}
+
+
+if __name__ == "__main__":
+    main()

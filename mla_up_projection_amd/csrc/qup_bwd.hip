@@ -47,6 +47,10 @@ __global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, float
   __syncthreads();
   const int n0 = blockIdx.x * IR_COLS + threadIdx.x * 8;
   if (n0 >= p.N) return;
+  const uint16_t* __restrict__ dq = p.dq;
+  uint16_t* __restrict__ dq_pre = p.dq_pre;
+  const float* __restrict__ cos_t = p.cos;
+  const float* __restrict__ sin_t = p.sin;
   const int d0 = n0 % p.D;  // 8 consecutive columns stay inside one head
   bool rot[4];
   int pi[4];
@@ -56,32 +60,51 @@ __global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, float
     rot[k] = p.d_rope > 0 && d >= p.d_nope;
     pi[k] = rot[k] ? (d - p.d_nope) >> 1 : 0;
   }
+  const bool any_rot = rot[0] || rot[1] || rot[2] || rot[3];
   float sum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int i = 0; i < rows; ++i) {
-    const int64_t t = r0 + i;
-    const u32x4_t g = *reinterpret_cast<const u32x4_t*>(p.dq + t * p.N + n0);
-    const int pos = s_pos[i];
-    const bool pos_ok = pos >= 0 && pos < p.rope_rows;
-    const int64_t trow = (int64_t)(pos_ok ? pos : 0) * p.rope_pairs;
-    uint32_t o[4];
+  // Rows in batches of RB: all loads of a batch are issued before any store,
+  // so RB 16-byte loads per lane are in flight at once.
+  constexpr int RB = 8;
+  for (int i0 = 0; i0 < rows; i0 += RB) {
+    u32x4_t g[RB];
+    float cs[RB][4], sn[RB][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float a = bf16_bits_to_f32(g[k] & 0xFFFFu);
-      float b = bf16_bits_to_f32(g[k] >> 16);
-      if (rot[k]) {
-        float c = p.cos[trow + pi[k]];
-        float s = p.sin[trow + pi[k]];
-        if (!pos_ok) c = s = __builtin_nanf("");
-        const float na = a * c + b * s;
-        const float nb = b * c - a * s;
-        a = na;
-        b = nb;
+    for (int j = 0; j < RB; ++j) {
+      const int i = i0 + j < rows ? i0 + j : rows - 1;
+      g[j] = *reinterpret_cast<const u32x4_t*>(dq + (r0 + i) * p.N + n0);
+      if (any_rot) {
+        const int pos = s_pos[i];
+        const bool pos_ok = pos >= 0 && pos < p.rope_rows;
+        const int64_t trow = (int64_t)(pos_ok ? pos : 0) * p.rope_pairs;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          cs[j][k] = rot[k] ? cos_t[trow + pi[k]] : 1.0f;
+          sn[j][k] = rot[k] ? sin_t[trow + pi[k]] : 0.0f;
+          if (!pos_ok) cs[j][k] = sn[j][k] = __builtin_nanf("");
+        }
       }
-      sum[2 * k] += a;
-      sum[2 * k + 1] += b;
-      o[k] = pack_bf16x2(a, b);
     }
-    *reinterpret_cast<u32x4_t*>(p.dq_pre + t * p.N + n0) = u32x4_t{o[0], o[1], o[2], o[3]};
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      if (i0 + j >= rows) break;
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float a = bf16_bits_to_f32(g[j][k] & 0xFFFFu);
+        float b = bf16_bits_to_f32(g[j][k] >> 16);
+        if (any_rot && rot[k]) {
+          const float c = cs[j][k], s = sn[j][k];
+          const float na = a * c + b * s;
+          const float nb = b * c - a * s;
+          a = na;
+          b = nb;
+        }
+        sum[2 * k] += a;
+        sum[2 * k + 1] += b;
+        o[k] = pack_bf16x2(a, b);
+      }
+      *reinterpret_cast<u32x4_t*>(dq_pre + (r0 + i0 + j) * p.N + n0) = u32x4_t{o[0], o[1], o[2], o[3]};
+    }
   }
   if (db_part) {
     float* dst = db_part + (int64_t)blockIdx.y * p.N + n0;
@@ -90,13 +113,26 @@ __global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, float
   }
 }
 
+// db[n] = sum of the per-chunk partials, in chunk order: 8 lanes per column
+// each add every 8th chunk, then the 8 partial sums are added in lane order.
+constexpr int DBR_COLS = 32;
 __global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict__ part, int chunks,
                                                        int N, uint16_t* __restrict__ db) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
+  __shared__ float red[8][DBR_COLS];
+  const int c = threadIdx.x % DBR_COLS;
+  const int g = threadIdx.x / DBR_COLS;
+  const int n = blockIdx.x * DBR_COLS + c;
   float s = 0.0f;
-  for (int c = 0; c < chunks; ++c) s += part[(int64_t)c * N + n];
-  db[n] = (uint16_t)f32_to_bf16_bits(s);
+  if (n < N)
+    for (int k = g; k < chunks; k += 8) s += part[(int64_t)k * N + n];
+  red[g][c] = s;
+  __syncthreads();
+  if (g == 0 && n < N) {
+    float t = red[0][c];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) t += red[q][c];
+    db[n] = (uint16_t)f32_to_bf16_bits(t);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -368,7 +404,7 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     if (e != hipSuccess) return e;
   }
   if (p.use_bias) {
-    hipLaunchKernelGGL(db_reduce_kernel, dim3((p.N + 255) / 256), dim3(256), 0, stream, db_part,
+    hipLaunchKernelGGL(db_reduce_kernel, dim3((p.N + DBR_COLS - 1) / DBR_COLS), dim3(256), 0, stream, db_part,
                        pl.db_row_chunks, p.N, p.db);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

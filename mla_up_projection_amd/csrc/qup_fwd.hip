@@ -16,6 +16,8 @@
 // runs of 4 consecutive head-dim elements of one token: RoPE pairs are
 // lane-local and a 32-element scale block is split between lanes l and
 // l^32 (one xor-shuffle for its amax).
+#include <utility>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -201,6 +203,26 @@ __device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokenMa
       reinterpret_cast<u32x4_t*>(dst)[1] = o1;
     }
   }
+}
+
+// The epilogue body is too large for the loop unroller, and a runtime index
+// into the accumulator array would place it in scratch memory; a fold over a
+// compile-time index sequence keeps every accumulator access constant.
+template <int I>
+__device__ __forceinline__ void epilogue_one(const FwdParams& p, const TokenMap& tm,
+                                             const f32x16_t (&acc)[WBLK_N][WBLK_T], int n_wave,
+                                             int64_t t_lane, int lane) {
+  constexpr int nb = I / WBLK_T;
+  constexpr int tb = I % WBLK_T;
+  const int n_blk = n_wave + 32 * nb;
+  if (n_blk < p.N) epilogue_block(p, tm, acc[nb][tb], n_blk, t_lane + 32 * tb, lane);
+}
+
+template <int... Is>
+__device__ __forceinline__ void epilogue_all(const FwdParams& p, const TokenMap& tm,
+                                             const f32x16_t (&acc)[WBLK_N][WBLK_T], int n_wave,
+                                             int64_t t_lane, int lane, std::integer_sequence<int, Is...>) {
+  (epilogue_one<Is>(p, tm, acc, n_wave, t_lane, lane), ...);
 }
 
 enum { MODE_BF16 = 0, MODE_MX_EXACT = 1, MODE_MX_FP8 = 2 };
@@ -449,16 +471,8 @@ __device__ __forceinline__ void run_tile(const FwdParams& p, uint8_t* lds) {
   }
 
   const TokenMap tm{p.fmt, p.B, p.S, p.cu, p.nseq};
-#pragma unroll
-  for (int nb = 0; nb < WBLK_N; ++nb) {
-    const int n_blk = n0 + wn * 96 + 32 * nb;
-    if (n_blk >= p.N) continue;  // uniform across the wave
-#pragma unroll
-    for (int tb = 0; tb < WBLK_T; ++tb) {
-      const int64_t t = t0 + wt * 128 + 32 * tb + (lane & 31);
-      epilogue_block(p, tm, acc[nb][tb], n_blk, t, lane);
-    }
-  }
+  epilogue_all(p, tm, acc, n0 + wn * 96, t0 + wt * 128 + (lane & 31), lane,
+               std::make_integer_sequence<int, WBLK_N * WBLK_T>{});
 }
 
 template <int MODE>
