@@ -103,6 +103,21 @@ void fill_token_map(const mla_tokens& tk, int& fmt, int& B, int& S, const int32_
 
 }  // namespace
 
+namespace mla {
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+}  // namespace mla
+
 extern "C" {
 
 const char* mla_status_str(mla_status s) {
@@ -164,6 +179,7 @@ mla_status mla_qup_fwd(const mla_qup_fwd_args* a, void* stream) {
   const bool mx_in = a->x_dtype == MLA_DTYPE_MXFP8;
   const bool mx_out = a->out_dtype == MLA_DTYPE_MXFP8;
   if (mx_in && a->K % 128 != 0) return MLA_EINVAL;
+  if (mx_in && !mla::fwd_scales_fit(a->K)) return MLA_EUNSUPPORTED;
   if ((st = check_rope(a->rope, a->d_rope, max_pos))) return st;
   const int64_t T = a->tokens.T;
   if (T == 0) return MLA_OK;
@@ -176,6 +192,9 @@ mla_status mla_qup_fwd(const mla_qup_fwd_args* a, void* stream) {
   const int D = a->d_nope + a->d_rope;
   const int64_t N = (int64_t)a->H * D;
   const size_t ein = mx_in ? 1 : 2;
+  // the forward kernel addresses X and W rows with 32-bit byte offsets
+  if ((uint64_t)T * a->K * ein > 0xFFFFFFFFull || (uint64_t)N * a->K * ein > 0xFFFFFFFFull)
+    return MLA_EUNSUPPORTED;
   const size_t eout = mx_out ? 1 : 2;
   std::vector<Range> ins = {rng(a->x, (size_t)T * a->K * ein), rng(a->w, (size_t)N * a->K * ein)};
   if (mx_in) {

@@ -35,8 +35,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // ---------------------------------------------------------------------------
 // MXFP8 (OCP Microscaling Formats v1.0, E4M3 elements, E8M0 scales).
-// Both helpers work on the float32 bit pattern with integer arithmetic only,
-// so results do not depend on the denormal mode of the floating-point unit.
+// The block exponent comes from the float32 bit pattern of amax by integer
+// arithmetic, so it does not depend on the denormal mode of the FP unit.
 // ---------------------------------------------------------------------------
 
 // |x| bit pattern; integer max over a block gives the bits of amax for finite
@@ -54,50 +54,25 @@ __device__ __forceinline__ int mx_block_exp(uint32_t amax_bits) {
   return e < -127 ? -127 : e;
 }
 
-// E4M3 code of x * 2^-E: round to nearest, ties to even, saturating to
-// +-448, sign of zero kept. x must be finite.
-//   value of x = M * 2^q (M the 24-bit significand with its hidden bit);
-//   L = floor(log2 |y|) for y = x * 2^-E;  the E4M3 spacing at y is
-//   2^(max(L,-6) - 3);  R = y / spacing rounded to nearest even;
-//   normal range: code = ((L+7) << 3) + (R - 8)  (R = 16 carries into the
-//   exponent field by itself); subnormal range (L < -6): code = R.
-__device__ __forceinline__ uint32_t e4m3_encode(float x, int E) {
-  uint32_t u = __float_as_uint(x);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  if (a == 0) return sign;
-  int ev = (int)(a >> 23);
-  uint32_t M = a & 0x7FFFFFu;
-  int q;
-  if (ev == 0) {
-    q = -149;
-  } else {
-    M |= 0x800000u;
-    q = ev - 150;
-  }
-  int msb = 31 - __clz(M);
-  int L = msb + q - E;
-  int ulp_e = (L < -6 ? -6 : L) - 3;
-  int shift = ulp_e - (q - E);
-  uint32_t R;
-  if (shift <= 0) {
-    R = M << (-shift);  // y / spacing < 16 here, so this cannot overflow
-  } else if (shift > 25) {
-    R = 0;              // M < 2^24 <= half a spacing
-  } else {
-    uint32_t keep = M >> shift;
-    uint32_t rem = M & ((1u << shift) - 1u);
-    uint32_t half = 1u << (shift - 1);
-    R = keep + ((rem > half || (rem == half && (keep & 1u))) ? 1u : 0u);
-  }
-  uint32_t code;
-  if (L < -6) {
-    code = R;
-  } else {
-    int c = ((L + 7) << 3) + (int)R - 8;
-    code = c > 0x7E ? 0x7Eu : (uint32_t)c;
-  }
-  return sign | code;
+// Four E4M3 codes (little-endian bytes of the result) of x0..x3 * 2^-E with
+// gfx950's scaled convert. v_cvt_scalef32_pk_fp8_f32 computes
+// fp8(x / scale) with round-to-nearest-even but does not saturate (values
+// past the last rounding boundary, 464, become NaN), so inputs are first
+// clamped to +-448 * 2^E: the OCP MX rule, saturating at the largest normal.
+// Requires finite inputs and -127 <= E <= 119.
+typedef short v2i16_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, float x3, int E) {
+  const float scale = __uint_as_float(E > -127 ? (uint32_t)(E + 127) << 23 : 0x00400000u);
+  const float lim = __uint_as_float(((uint32_t)(E + 135) << 23) | 0x00600000u);  // 1.75 * 2^(E+8)
+  x0 = fminf(fmaxf(x0, -lim), lim);
+  x1 = fminf(fmaxf(x1, -lim), lim);
+  x2 = fminf(fmaxf(x2, -lim), lim);
+  x3 = fminf(fmaxf(x3, -lim), lim);
+  v2i16_t o = {0, 0};
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, x0, x1, scale, false);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, x2, x3, scale, true);
+  return __builtin_bit_cast(uint32_t, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -112,24 +87,25 @@ struct TokenMap {
 
 __device__ __forceinline__ void token_coords(const TokenMap& tm, int64_t t, int& pos, int& b,
                                              int& s) {
+  const int t32 = (int)t;  // T < 2^31 (validated by the C ABI)
   if (tm.fmt == FMT_BSHD) {
-    b = (int)(t / tm.S);
-    s = (int)(t - (int64_t)b * tm.S);
+    b = t32 / tm.S;
+    s = t32 - b * tm.S;
     pos = s;
   } else if (tm.fmt == FMT_SBHD) {
-    s = (int)(t / tm.B);
-    b = (int)(t - (int64_t)s * tm.B);
+    s = t32 / tm.B;
+    b = t32 - s * tm.B;
     pos = s;
   } else {
     // largest j with cu[j] <= t (binary search over nseq+1 entries)
     int lo = 0, hi = tm.nseq;
     while (hi - lo > 1) {
       int mid = (lo + hi) >> 1;
-      if ((int64_t)tm.cu[mid] <= t) lo = mid; else hi = mid;
+      if (tm.cu[mid] <= t32) lo = mid; else hi = mid;
     }
-    pos = (int)(t - tm.cu[lo]);
+    pos = t32 - tm.cu[lo];
     b = 0;
-    s = (int)t;
+    s = t32;
   }
 }
 

@@ -52,11 +52,8 @@ __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const void* __restrict
       sc = 0xFF;
     } else {
       const int E = mx_block_exp(m);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c0 |= e4m3_encode(v[i], E) << (8 * i);
-        c1 |= e4m3_encode(v[4 + i], E) << (8 * i);
-      }
+      c0 = e4m3_pack4(v[0], v[1], v[2], v[3], E);
+      c1 = e4m3_pack4(v[4], v[5], v[6], v[7], E);
       sc = (uint32_t)(E + 127);
     }
     *reinterpret_cast<uint2*>(codes + row * cols + col) = make_uint2(c0, c1);

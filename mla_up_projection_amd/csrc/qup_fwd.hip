@@ -1,21 +1,31 @@
 // Fused MLA query up-projection forward for gfx950:
-//   Q^T tile = W_tile * X_tile^T on MFMA (bf16 32x32x16, or the scaled FP8
-//   32x32x64 for MXFP8 operands), then a register-level epilogue: bias,
-//   RoPE/YaRN rotation of each head's rope slice, per-32 amax, E8M0 scale,
-//   E4M3 encode (or bf16), BHSD store with scales laid out like the data.
+//   Q^T tile = W_tile * X_tile^T on MFMA, then a register-level epilogue:
+//   bias, RoPE/YaRN rotation of each head's rope slice, per-32 amax, E8M0
+//   scale, E4M3 encode (or bf16), BHSD store with scales laid out like the
+//   data.
 // Pages: "Add support for fused Q Up-Proj GEMM/RoPE/Quant." (description,
 // flowchart: GEMM + RoPE + MXFP8 quantization in one kernel, 16-bit or MXFP8
 // projection, BHSD scale transpose); "Fix fused MLA YaRN RoPE query kernel
 // corrupting upstream tensor in-place" (the rotation is out of place: the
 // accumulator is rotated in registers, no intermediate q exists).
 //
-// Tile: 192 rows of N (six 32-row blocks; a block never straddles a head
-// because D is a multiple of 32) x 256 tokens, 4 waves in a 2 x 2 grid, each
-// wave 96 rows x 128 tokens = 3 x 4 MFMA blocks. The MFMA row axis is N
-// (W is the A operand), so in the 32x32 accumulator layout a lane holds
-// runs of 4 consecutive head-dim elements of one token: RoPE pairs are
-// lane-local and a 32-element scale block is split between lanes l and
-// l^32 (one xor-shuffle for its amax).
+// Work decomposition (one 256-thread workgroup per CU, persistent):
+//   * tile = 256 tokens x 256 rows of N; 4 waves in 2 x 2, each wave owns
+//     128 rows x 128 tokens = 4 x 4 blocks of the 32x32 MFMA, 256 fp32
+//     accumulators per lane. The MFMA row axis is N (W is the A operand), so
+//     a lane holds runs of 4 consecutive head-dim elements of one token:
+//     RoPE pairs are lane-local and a 32-element scale block is split
+//     between lanes l and l^32 (one xor-shuffle for its amax).
+//   * K streams through a 3-slot LDS ring of 64-byte row slices (32 bf16 or
+//     64 E4M3 K-values per row per stage), filled by direct global->LDS DMA
+//     (global_load_lds_dwordx4) issued two stages ahead; each wave counts
+//     its own outstanding DMA with s_waitcnt vmcnt and one s_barrier per
+//     stage publishes the slot. The main loop issues no other vector-memory
+//     instruction, so the counts are exact.
+//   * After the last stage of a tile, the first stages of the workgroup's
+//     next tile are put in flight before the epilogue runs.
+//   * Tiles are ordered so that the 32 workgroups resident on one XCD share
+//     W and X slices in that XCD's L2.
 #include <utility>
 
 #include "device_common.h"
@@ -24,97 +34,79 @@
 namespace mla {
 namespace {
 
-constexpr int TILE_N = 192;
 constexpr int TILE_T = 256;
-constexpr int ROW_BYTES = 128;            // bytes of one tile row per LDS stage
-constexpr int NWAVES = 4;
-constexpr int NTHREADS = NWAVES * 64;
-constexpr int WBLK_N = 3;                 // 32-row blocks per wave
+constexpr int TILE_N = 256;
+constexpr int NTHREADS = 256;
+constexpr int ROWB = 64;                  // bytes of one tile row per stage
+constexpr int XSB = TILE_T * ROWB;        // X part of a stage (16 KB)
+constexpr int WSB = TILE_N * ROWB;        // W part of a stage (16 KB)
+constexpr int SB = XSB + WSB;             // one ring slot (32 KB)
+constexpr int STAGES = 3;
+constexpr int RING = SB * STAGES;         // 96 KB
+constexpr int LQ = TILE_T / 64;           // DMA loads per wave per operand per stage
+constexpr int LPS = 2 * LQ;               // DMA loads per wave per stage
+constexpr int WBLK_N = 4;                 // 32-row blocks per wave
 constexpr int WBLK_T = 4;                 // 32-token blocks per wave
-constexpr int X_STAGE = TILE_T * ROW_BYTES;
-constexpr int W_STAGE = TILE_N * ROW_BYTES;
-constexpr int STAGE = X_STAGE + W_STAGE;  // 57344 bytes
-constexpr int LDS_BYTES = 2 * STAGE;      // double buffered
-constexpr int X_CHUNKS = TILE_T * 8 / NTHREADS;   // 16-byte chunks per thread
-constexpr int W_CHUNKS = TILE_N * 8 / NTHREADS;
+constexpr int MAX_SCALE_BYTES = 16 * 1024;  // LDS for the MXFP8 operand scales of a tile
 
-// LDS address of 16-byte chunk c of row r: chunks are xor-swizzled with the
-// row's low 3 bits so that 8 lanes reading one chunk column of 8 rows hit
-// 8 distinct bank groups.
-__device__ __forceinline__ int lds_off(int r, int c) { return r * ROW_BYTES + ((c ^ (r & 7)) << 4); }
+// Chunk swizzle of a 64-byte row (four 16-byte chunks): chunk c of row r is
+// stored at c ^ ((r >> 2) & 3), so that the 16 lanes of a fragment read that
+// hit 16 consecutive rows spread over all bank groups.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int roff(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
 
-// Grid position -> (token tile, n tile). Workgroups are dispatched round
-// robin over the 8 XCDs; consecutive ids on one XCD are given the same
-// W tile and successive token tiles so they share the W rows in that XCD's
-// L2 while walking X.
-__device__ __forceinline__ void tile_of(int g, int tiles_t, int tiles_n, int& tt, int& tn) {
-  const int total = tiles_t * tiles_n;
-  int id = g;
-  if ((total & 7) == 0) id = (g & 7) * (total >> 3) + (g >> 3);
-  tt = id % tiles_t;
-  tn = id / tiles_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Direct global->LDS copy of 16 bytes per lane: lane i of the wave writes
+// LDS bytes [lds_addr + 16 i, +16) from global sbase + voff.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(sbase)
+               : "memory", "m0");
 }
 
-struct Staging {
-  u32x4_t x[X_CHUNKS];
-  u32x4_t w[W_CHUNKS];
-};
-
-// Global -> registers for one LDS stage: 128 bytes of every tile row,
-// starting at byte column kb0 of X and W rows (row pitch row_bytes).
-__device__ __forceinline__ void load_stage(Staging& st, const uint8_t* __restrict__ xb,
-                                           const uint8_t* __restrict__ wb, int64_t t0, int n0,
-                                           int64_t T, int N, int64_t row_bytes, int64_t kb0,
-                                           int tid) {
-  const int c = tid & 7;
-  const bool kin = kb0 + c * 16 < row_bytes;
-#pragma unroll
-  for (int i = 0; i < X_CHUNKS; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    const int64_t t = t0 + r;
-    if (kin && t < T)
-      st.x[i] = *reinterpret_cast<const u32x4_t*>(xb + t * row_bytes + kb0 + c * 16);
-    else
-      st.x[i] = u32x4_t{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int i = 0; i < W_CHUNKS; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    const int n = n0 + r;
-    if (kin && n < N)
-      st.w[i] = *reinterpret_cast<const u32x4_t*>(wb + (int64_t)n * row_bytes + kb0 + c * 16);
-    else
-      st.w[i] = u32x4_t{0, 0, 0, 0};
-  }
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-__device__ __forceinline__ void store_stage(const Staging& st, uint8_t* lds, int tid) {
-  const int c = tid & 7;
-#pragma unroll
-  for (int i = 0; i < X_CHUNKS; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    *reinterpret_cast<u32x4_t*>(lds + lds_off(r, c)) = st.x[i];
-  }
-#pragma unroll
-  for (int i = 0; i < W_CHUNKS; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    *reinterpret_cast<u32x4_t*>(lds + X_STAGE + lds_off(r, c)) = st.w[i];
-  }
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
 }
 
 // ---------------------------------------------------------------------------
 // Fused epilogue for one 32 (n) x 32 (token) accumulator block.
 // acc[r] holds row 8*(r/4) + 4*(lane/32) + r%4 of the block, token lane%32.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokenMap& tm,
-                                               const f32x16_t& acc, int n_blk, int64_t t,
-                                               int lane) {
+struct TokInfo {
+  bool ok;      // token row < T
+  int pos;      // RoPE position
+  int64_t row;  // BHSD row of head 0: (b*H)*S + s; head h adds h*S
+};
+
+__device__ __forceinline__ TokInfo tok_info(const FwdParams& p, const TokenMap& tm, int64_t t) {
+  TokInfo ti{t < p.T, 0, 0};
+  if (ti.ok) {
+    int b, s;
+    token_coords(tm, t, ti.pos, b, s);
+    ti.row = (int64_t)b * p.H * p.S + s;
+  }
+  return ti;
+}
+
+__device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokInfo& ti, const f32x16_t& acc,
+                                               int n_blk, int lane) {
   const int half = lane >> 5;
-  const bool tok_ok = t < p.T;
   const int h = n_blk / p.D;
   const int d_blk = n_blk - h * p.D;
-  int pos = 0, b = 0, s = 0;
-  if (tok_ok) token_coords(tm, t, pos, b, s);
 
   float v[16];
 #pragma unroll
@@ -128,8 +120,8 @@ __device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokenMa
     }
   }
   if (d_blk + 32 > p.d_nope && p.d_rope > 0) {
-    const bool pos_ok = tok_ok && pos >= 0 && pos < p.rope_rows;
-    const int64_t trow = (int64_t)(pos_ok ? pos : 0) * p.rope_pairs;
+    const bool pos_ok = ti.ok && ti.pos >= 0 && ti.pos < p.rope_rows;
+    const int64_t trow = (int64_t)(pos_ok ? ti.pos : 0) * p.rope_pairs;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const int d = d_blk + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -145,7 +137,7 @@ __device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokenMa
     }
   }
 
-  const int64_t row = ((int64_t)b * p.H + h) * p.S + s;  // BHSD (b, h, s)
+  const int64_t row = ti.row + (int64_t)h * p.S;  // BHSD (b, h, s)
   if (p.out_mx) {
     uint32_t m = 0;
 #pragma unroll
@@ -159,10 +151,7 @@ __device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokenMa
     } else {
       const int E = mx_block_exp(m);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        P[g] = e4m3_encode(v[4 * g + 0], E) | (e4m3_encode(v[4 * g + 1], E) << 8) |
-               (e4m3_encode(v[4 * g + 2], E) << 16) | (e4m3_encode(v[4 * g + 3], E) << 24);
-      }
+      for (int g = 0; g < 4; ++g) P[g] = e4m3_pack4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], E);
       sc = (uint32_t)(E + 127);
     }
     // Lanes l and l+32 swap two 4-row groups so each ends up with 16
@@ -172,7 +161,7 @@ __device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokenMa
     const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32);
     const uint32_t r1 = (uint32_t)__shfl_xor((int)s1, 32);
     u32x4_t o = half ? u32x4_t{r0, P[2], r1, P[3]} : u32x4_t{P[0], r0, P[1], r1};
-    if (tok_ok) {
+    if (ti.ok) {
       uint8_t* dst = static_cast<uint8_t*>(p.out) + row * p.D + d_blk + 16 * half;
       *reinterpret_cast<u32x4_t*>(dst) = o;
       if (half == 0) p.out_scales[row * (p.D / 32) + d_blk / 32] = (uint8_t)sc;
@@ -197,7 +186,7 @@ __device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokenMa
       o0 = u32x4_t{P[0], P[1], rcv[0], rcv[1]};
       o1 = u32x4_t{P[2], P[3], rcv[2], rcv[3]};
     }
-    if (tok_ok) {
+    if (ti.ok) {
       uint16_t* dst = static_cast<uint16_t*>(p.out) + row * p.D + d_blk + 16 * half;
       reinterpret_cast<u32x4_t*>(dst)[0] = o0;
       reinterpret_cast<u32x4_t*>(dst)[1] = o1;
@@ -209,80 +198,97 @@ __device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokenMa
 // into the accumulator array would place it in scratch memory; a fold over a
 // compile-time index sequence keeps every accumulator access constant.
 template <int I>
-__device__ __forceinline__ void epilogue_one(const FwdParams& p, const TokenMap& tm,
-                                             const f32x16_t (&acc)[WBLK_N][WBLK_T], int n_wave,
-                                             int64_t t_lane, int lane) {
+__device__ __forceinline__ void epilogue_one(const FwdParams& p, const TokInfo (&ti)[WBLK_T],
+                                             const f32x16_t (&acc)[WBLK_N][WBLK_T], int n_wave, int lane) {
   constexpr int nb = I / WBLK_T;
   constexpr int tb = I % WBLK_T;
   const int n_blk = n_wave + 32 * nb;
-  if (n_blk < p.N) epilogue_block(p, tm, acc[nb][tb], n_blk, t_lane + 32 * tb, lane);
+  // one block at a time: interleaving blocks would hold several blocks'
+  // temporaries live next to the 256 accumulators
+  __builtin_amdgcn_sched_barrier(0);
+  if (n_blk < p.N) epilogue_block(p, ti[tb], acc[nb][tb], n_blk, lane);
 }
 
 template <int... Is>
 __device__ __forceinline__ void epilogue_all(const FwdParams& p, const TokenMap& tm,
                                              const f32x16_t (&acc)[WBLK_N][WBLK_T], int n_wave,
                                              int64_t t_lane, int lane, std::integer_sequence<int, Is...>) {
-  (epilogue_one<Is>(p, tm, acc, n_wave, t_lane, lane), ...);
+  TokInfo ti[WBLK_T];
+#pragma unroll
+  for (int tb = 0; tb < WBLK_T; ++tb) ti[tb] = tok_info(p, tm, t_lane + 32 * tb);
+  (epilogue_one<Is>(p, ti, acc, n_wave, lane), ...);
+}
+
+// ---------------------------------------------------------------------------
+// Tile scheduling.
+// ---------------------------------------------------------------------------
+struct TileGrid {
+  int tiles_t, tiles_n, total;
+};
+
+// Tile u -> (token tile, n tile). Workgroup g runs on XCD g % 8 and takes
+// tiles g, g + G, g + 2G, ... (G a multiple of 8), so every tile of one XCD
+// has u % 8 == xcd. Each XCD owns a contiguous run of the n-major tile order;
+// in one round its 32 resident workgroups cover 16 token tiles of 2 n tiles.
+__device__ __forceinline__ void tile_coords(const TileGrid& g, int u, int& tt, int& tn) {
+  int v = u;
+  if ((g.total & 7) == 0) v = (u & 7) * (g.total >> 3) + (u >> 3);
+  tt = v % g.tiles_t;
+  tn = v / g.tiles_t;
 }
 
 enum { MODE_BF16 = 0, MODE_MX_EXACT = 1, MODE_MX_FP8 = 2 };
 
-// MXFP8 operands, exact mode: per LDS stage of 64 K-values, each thread
-// loads 16-byte runs of E4M3 codes (16 K-values of one row, inside one
-// 32-block), converts them to bf16 with the block's E8M0 scale folded in
-// (v_cvt_scalef32_pk_bf16_fp8: code * 2^(scale-127), exact whenever the
-// result is a bf16 normal), and stores two bf16 chunks, so the stage has the
-// layout of the bf16 path. E4M3 values have 4 significant bits, so products
-// of two are exact in fp32 and the bf16 MFMA accumulates them in fp32.
-constexpr int MXE_X = TILE_T * 4 / NTHREADS;  // 16-byte code runs per thread
-constexpr int MXE_W = TILE_N * 4 / NTHREADS;
-
-struct MxStaging {
-  u32x4_t x[MXE_X];
-  u32x4_t w[MXE_W];
-  uint32_t xs[MXE_X];
-  uint32_t ws[MXE_W];
+template <int MODE>
+struct Tile {
+  static constexpr bool MX = MODE != MODE_BF16;
+  // K-values per stage: 32 bf16 or 64 E4M3 per 64-byte row slice
+  static constexpr int KPS = MX ? 64 : 32;
 };
 
-__device__ __forceinline__ void load_stage_mx(MxStaging& st, const FwdParams& p, int64_t t0, int n0,
-                                              int kt, int tid) {
-  const int c16 = tid & 3;
-  const int kb = 64 * kt + 16 * c16;  // first K index of this run
-  const int kblocks = p.K / 32;
-  const uint8_t* xb = static_cast<const uint8_t*>(p.x);
-  const uint8_t* wb = static_cast<const uint8_t*>(p.w);
+// Per-lane DMA source offsets of one tile (rows clamped into the matrix so
+// that partial tiles never read out of bounds; clamped rows only feed
+// accumulators the epilogue discards).
+struct DmaPlan {
+  uint32_t xo[LQ];
+  uint32_t wo[LQ];
+};
+
+__device__ __forceinline__ DmaPlan dma_plan(const FwdParams& p, int64_t t0, int n0, int wave, int lane,
+                                           int row_bytes) {
+  DmaPlan d;
+  const int lr = lane >> 2;
+  const int c = (lane & 3) ^ swz(lr);
 #pragma unroll
-  for (int i = 0; i < MXE_X; ++i) {
-    const int r = (tid >> 2) + 64 * i;
-    const int64_t t = t0 + r;
-    if (t < p.T) {
-      st.x[i] = *reinterpret_cast<const u32x4_t*>(xb + t * p.K + kb);
-      st.xs[i] = p.xs[t * kblocks + (kb >> 5)];
-    } else {
-      st.x[i] = u32x4_t{0, 0, 0, 0};
-      st.xs[i] = 127;
-    }
+  for (int q = 0; q < LQ; ++q) {
+    const int r = 16 * (4 * q + wave) + lr;
+    int64_t t = t0 + r;
+    if (t >= p.T) t = p.T - 1;
+    int n = n0 + r;
+    if (n >= p.N) n = p.N - 1;
+    d.xo[q] = (uint32_t)(t * row_bytes + c * 16);
+    d.wo[q] = (uint32_t)((int64_t)n * row_bytes + c * 16);
   }
-#pragma unroll
-  for (int i = 0; i < MXE_W; ++i) {
-    const int r = (tid >> 2) + 64 * i;
-    const int n = n0 + r;
-    if (n < p.N) {
-      st.w[i] = *reinterpret_cast<const u32x4_t*>(wb + (int64_t)n * p.K + kb);
-      st.ws[i] = p.ws[(int64_t)n * kblocks + (kb >> 5)];
-    } else {
-      st.w[i] = u32x4_t{0, 0, 0, 0};
-      st.ws[i] = 127;
-    }
-  }
+  return d;
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Stage `kt` of the tile (K slice kt, clamped to the last one) into ring
+// slot `slot_kt % STAGES`.
+__device__ __forceinline__ void issue_stage(const DmaPlan& d, const uint8_t* xb, const uint8_t* wb,
+                                            int kt, int nk, int slot_kt, uint32_t ring, int wave) {
+  const uint32_t slot = ring + (uint32_t)(slot_kt % STAGES) * SB;
+  const int64_t kb = (int64_t)(kt < nk ? kt : nk - 1) * ROWB;
+#pragma unroll
+  for (int q = 0; q < LQ; ++q) dma16(xb + kb, d.xo[q], slot + (4 * q + wave) * 1024);
+#pragma unroll
+  for (int q = 0; q < LQ; ++q) dma16(wb + kb, d.wo[q], slot + XSB + (4 * q + wave) * 1024);
+}
 
-template <bool HI>
-__device__ __forceinline__ uint32_t cvt2(uint32_t codes, float scale) {
-  const bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, scale, HI);
-  return __builtin_bit_cast(uint32_t, v);
+// Four E4M3 codes -> four bf16 (two dwords), each times 2^(scale - 127).
+__device__ __forceinline__ u32x2_t cvt4(uint32_t codes, float scale) {
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, scale, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, scale, true);
+  return u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 // 2^(e8m0 - 127) as a float (byte 0 gives the float32 subnormal 2^-127).
@@ -290,215 +296,227 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(s ? (s << 23) : 0x00400000u);
 }
 
-__device__ __forceinline__ void store_run(uint8_t* lds, int r, int c16, const u32x4_t& v, uint32_t sbyte) {
-  const float sc = e8m0_to_f32(sbyte);
-  const u32x4_t lo = u32x4_t{cvt2<false>(v[0], sc), cvt2<true>(v[0], sc), cvt2<false>(v[1], sc),
-                             cvt2<true>(v[1], sc)};
-  const u32x4_t hi = u32x4_t{cvt2<false>(v[2], sc), cvt2<true>(v[2], sc), cvt2<false>(v[3], sc),
-                             cvt2<true>(v[3], sc)};
-  *reinterpret_cast<u32x4_t*>(lds + lds_off(r, 2 * c16)) = lo;
-  *reinterpret_cast<u32x4_t*>(lds + lds_off(r, 2 * c16 + 1)) = hi;
+__device__ __forceinline__ bf16x8_t frag_mx_exact(const uint8_t* rowp, int j, int half, int r,
+                                                  float scale) {
+  // 8 codes: K-values 16 j + 8 half .. +7 of this row slice (chunk j)
+  const u32x2_t c = *reinterpret_cast<const u32x2_t*>(rowp + ((j ^ swz(r)) << 4) + 8 * half);
+  const u32x2_t lo = cvt4(c[0], scale);
+  const u32x2_t hi = cvt4(c[1], scale);
+  const u32x4_t v = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
-__device__ __forceinline__ void store_stage_mx(const MxStaging& st, uint8_t* lds, int tid) {
-  const int c16 = tid & 3;
+template <int MODE>
+__device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const uint8_t* cur,
+                                          const uint8_t* xsc, const uint8_t* wsc, int kblocks, int kt,
+                                          int arow0, int brow0, int half) {
+  if (MODE == MODE_BF16) {
 #pragma unroll
-  for (int i = 0; i < MXE_X; ++i) store_run(lds, (tid >> 2) + 64 * i, c16, st.x[i], st.xs[i]);
+    for (int j = 0; j < 2; ++j) {  // two k16 steps per 32-value slice
+      bf16x8_t a[WBLK_N], b[WBLK_T];
 #pragma unroll
-  for (int i = 0; i < MXE_W; ++i) store_run(lds + X_STAGE, (tid >> 2) + 64 * i, c16, st.w[i], st.ws[i]);
-}
-
-// bf16 MFMA over one LDS stage (64 K-values): 4 steps of k16.
-__device__ __forceinline__ void mma_stage_bf16(f32x16_t (&acc)[WBLK_N][WBLK_T], const uint8_t* cur,
-                                               int arow0, int brow0, int half) {
+      for (int nb = 0; nb < WBLK_N; ++nb)
+        a[nb] = *reinterpret_cast<const bf16x8_t*>(cur + XSB + roff(arow0 + 32 * nb, 2 * j + half));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ch = 2 * j + half;
-    bf16x8_t a[WBLK_N], bv[WBLK_T];
+      for (int tb = 0; tb < WBLK_T; ++tb)
+        b[tb] = *reinterpret_cast<const bf16x8_t*>(cur + roff(brow0 + 32 * tb, 2 * j + half));
 #pragma unroll
-    for (int nb = 0; nb < WBLK_N; ++nb)
-      a[nb] = *reinterpret_cast<const bf16x8_t*>(cur + X_STAGE + lds_off(arow0 + 32 * nb, ch));
+      for (int nb = 0; nb < WBLK_N; ++nb)
 #pragma unroll
-    for (int tb = 0; tb < WBLK_T; ++tb)
-      bv[tb] = *reinterpret_cast<const bf16x8_t*>(cur + lds_off(brow0 + 32 * tb, ch));
+        for (int tb = 0; tb < WBLK_T; ++tb)
+          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[tb], acc[nb][tb], 0, 0, 0);
+    }
+  } else if (MODE == MODE_MX_EXACT) {
+    // E4M3 expanded exactly to bf16 (code * 2^(scale-127)) per fragment; the
+    // bf16 MFMA then multiplies exactly and accumulates in fp32.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // four k16 steps per 64-value slice
+      const int kblk = 2 * kt + (j >> 1);
+      bf16x8_t a[WBLK_N], b[WBLK_T];
+#pragma unroll
+      for (int nb = 0; nb < WBLK_N; ++nb) {
+        const int r = arow0 + 32 * nb;
+        a[nb] = frag_mx_exact(cur + XSB + r * ROWB, j, half, r, e8m0_to_f32(wsc[r * kblocks + kblk]));
+      }
+#pragma unroll
+      for (int tb = 0; tb < WBLK_T; ++tb) {
+        const int r = brow0 + 32 * tb;
+        b[tb] = frag_mx_exact(cur + r * ROWB, j, half, r, e8m0_to_f32(xsc[r * kblocks + kblk]));
+      }
+#pragma unroll
+      for (int nb = 0; nb < WBLK_N; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < WBLK_T; ++tb)
+          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[tb], acc[nb][tb], 0, 0, 0);
+    }
+  } else {
+    // Scaled FP8 32x32x64: lane (row, half) holds 16 bytes of K-block 0
+    // (k = 16 half .. +15) in its first four registers and 16 bytes of
+    // K-block 1 (k = 32 + 16 half .. +15) in the last four; the E8M0 scale
+    // of (row, block b) is taken from lane row + 32 b, byte 0.
+    const int kblk = 2 * kt + half;
+    i32x8_t a[WBLK_N], b[WBLK_T];
+    uint32_t sa[WBLK_N], sb[WBLK_T];
+#pragma unroll
+    for (int nb = 0; nb < WBLK_N; ++nb) {
+      const int r = arow0 + 32 * nb;
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + XSB + roff(r, half));
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + XSB + roff(r, 2 + half));
+      a[nb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      sa[nb] = wsc[r * kblocks + kblk];
+    }
+#pragma unroll
+    for (int tb = 0; tb < WBLK_T; ++tb) {
+      const int r = brow0 + 32 * tb;
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + roff(r, half));
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + roff(r, 2 + half));
+      b[tb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      sb[tb] = xsc[r * kblocks + kblk];
+    }
 #pragma unroll
     for (int nb = 0; nb < WBLK_N; ++nb)
 #pragma unroll
       for (int tb = 0; tb < WBLK_T; ++tb)
-        acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], bv[tb], acc[nb][tb], 0, 0, 0);
+        acc[nb][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            a[nb], b[tb], acc[nb][tb], 0, 0, 0, (int)sa[nb], 0, (int)sb[tb]);
   }
 }
 
-template <int MODE>
-__device__ __forceinline__ void run_tile(const FwdParams& p, uint8_t* lds) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave >> 1;  // which 96-row half of the N tile
-  const int wt = wave & 1;   // which 128-token half of the token tile
-  const int tiles_t = (int)((p.T + TILE_T - 1) / TILE_T);
-  const int tiles_n = (p.N + TILE_N - 1) / TILE_N;
-  int tt, tn;
-  tile_of(blockIdx.x, tiles_t, tiles_n, tt, tn);
-  const int64_t t0 = (int64_t)tt * TILE_T;
-  const int n0 = tn * TILE_N;
-
-  f32x16_t acc[WBLK_N][WBLK_T];
-#pragma unroll
-  for (int i = 0; i < WBLK_N; ++i)
-#pragma unroll
-    for (int j = 0; j < WBLK_T; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // Fragment rows of this lane inside the tile.
-  const int arow0 = wn * 96 + (lane & 31);   // + 32*nb
-  const int brow0 = wt * 128 + (lane & 31);  // + 32*tb
-  const int half = lane >> 5;
-
-  if (MODE == MODE_MX_EXACT) {
-    const int nk = p.K / 64;
-    MxStaging st;
-    load_stage_mx(st, p, t0, n0, 0, tid);
-    store_stage_mx(st, lds, tid);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
-      if (more) load_stage_mx(st, p, t0, n0, kt + 1, tid);
-      mma_stage_bf16(acc, lds + (kt & 1) * STAGE, arow0, brow0, half);
-      if (more) store_stage_mx(st, lds + ((kt + 1) & 1) * STAGE, tid);
-      __syncthreads();
-    }
-  } else {
-    constexpr bool FP8 = MODE == MODE_MX_FP8;
-    const int64_t row_bytes = FP8 ? (int64_t)p.K : (int64_t)p.K * 2;
-    const int nk = (int)((row_bytes + ROW_BYTES - 1) / ROW_BYTES);
-    const uint8_t* xb = static_cast<const uint8_t*>(p.x);
-    const uint8_t* wb = static_cast<const uint8_t*>(p.w);
-
-    // FP8 MFMA: E8M0 scales of this lane's rows for the current stage (4
-    // blocks of 32 along K), pre-shifted so byte 0 / byte 2 serve MFMA step
-    // 0 / 1 (lane half h supplies the scale of K-block h of each step).
-    const int kblocks = p.K / 32;
-    uint32_t xsc[WBLK_T], wsc[WBLK_N], xsc_n[WBLK_T], wsc_n[WBLK_N];
-    auto load_scales = [&](int kt, uint32_t* xs_out, uint32_t* ws_out) {
-#pragma unroll
-      for (int tb = 0; tb < WBLK_T; ++tb) {
-        const int64_t t = t0 + brow0 + 32 * tb;
-        uint32_t v = 0;
-        if (t < p.T) {
-          const uint8_t* s = p.xs + t * kblocks + 4 * kt;
-          v = (uint32_t)s[0] | ((uint32_t)s[1] << 8) | ((uint32_t)s[2] << 16) | ((uint32_t)s[3] << 24);
-        }
-        xs_out[tb] = v >> (8 * half);
-      }
-#pragma unroll
-      for (int nb = 0; nb < WBLK_N; ++nb) {
-        const int n = n0 + arow0 + 32 * nb;
-        uint32_t v = 0;
-        if (n < p.N) {
-          const uint8_t* s = p.ws + (int64_t)n * kblocks + 4 * kt;
-          v = (uint32_t)s[0] | ((uint32_t)s[1] << 8) | ((uint32_t)s[2] << 16) | ((uint32_t)s[3] << 24);
-        }
-        ws_out[nb] = v >> (8 * half);
-      }
-    };
-
-    Staging st;
-    load_stage(st, xb, wb, t0, n0, p.T, p.N, row_bytes, 0, tid);
-    if (FP8) load_scales(0, xsc, wsc);
-    store_stage(st, lds, tid);
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
-      if (more) {
-        load_stage(st, xb, wb, t0, n0, p.T, p.N, row_bytes, (int64_t)(kt + 1) * ROW_BYTES, tid);
-        if (FP8) load_scales(kt + 1, xsc_n, wsc_n);
-      }
-      const uint8_t* cur = lds + (kt & 1) * STAGE;
-      if (!FP8) {
-        mma_stage_bf16(acc, cur, arow0, brow0, half);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {  // 2 steps of k64 per 128-byte stage
-          // Scaled FP8 32x32x64 operand: lane (row, half) holds 16 bytes of
-          // K-block 0 (k = 16*half .. +15) in its first four registers and 16
-          // bytes of K-block 1 (k = 32 + 16*half .. +15) in the last four; the
-          // E8M0 scale of (row, block b) is taken from lane row + 32*b.
-          const int ch = 4 * j + half;
-          i32x8_t a[WBLK_N], bv[WBLK_T];
-#pragma unroll
-          for (int nb = 0; nb < WBLK_N; ++nb) {
-            const int r = arow0 + 32 * nb;
-            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + X_STAGE + lds_off(r, ch));
-            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + X_STAGE + lds_off(r, ch + 2));
-            a[nb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          }
-#pragma unroll
-          for (int tb = 0; tb < WBLK_T; ++tb) {
-            const int r = brow0 + 32 * tb;
-            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + lds_off(r, ch));
-            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + lds_off(r, ch + 2));
-            bv[tb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          }
-#pragma unroll
-          for (int nb = 0; nb < WBLK_N; ++nb)
-#pragma unroll
-            for (int tb = 0; tb < WBLK_T; ++tb) {
-              if (j == 0)
-                acc[nb][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    a[nb], bv[tb], acc[nb][tb], 0, 0, 0, (int)wsc[nb], 0, (int)xsc[tb]);
-              else
-                acc[nb][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    a[nb], bv[tb], acc[nb][tb], 0, 0, 2, (int)wsc[nb], 2, (int)xsc[tb]);
-            }
-        }
-      }
-      if (more) {
-        store_stage(st, lds + ((kt + 1) & 1) * STAGE, tid);
-        if (FP8) {
-#pragma unroll
-          for (int tb = 0; tb < WBLK_T; ++tb) xsc[tb] = xsc_n[tb];
-#pragma unroll
-          for (int nb = 0; nb < WBLK_N; ++nb) wsc[nb] = wsc_n[nb];
-        }
-      }
-      __syncthreads();
-    }
+// MXFP8 operand scales of a tile (all K blocks of its 256 X rows and 256 W
+// rows) copied into LDS with ordinary loads, before the main loop.
+__device__ __forceinline__ void load_tile_scales(const FwdParams& p, int64_t t0, int n0, uint8_t* xsc,
+                                                 uint8_t* wsc, int tid) {
+  const int kb = p.K / 32;
+  for (int e = tid; e < TILE_T * kb; e += NTHREADS) {
+    const int r = e / kb, c = e - r * kb;
+    int64_t t = t0 + r;
+    if (t >= p.T) t = p.T - 1;
+    xsc[e] = p.xs[t * kb + c];
   }
-
-  const TokenMap tm{p.fmt, p.B, p.S, p.cu, p.nseq};
-  epilogue_all(p, tm, acc, n0 + wn * 96, t0 + wt * 128 + (lane & 31), lane,
-               std::make_integer_sequence<int, WBLK_N * WBLK_T>{});
+  for (int e = tid; e < TILE_N * kb; e += NTHREADS) {
+    const int r = e / kb, c = e - r * kb;
+    int n = n0 + r;
+    if (n >= p.N) n = p.N - 1;
+    wsc[e] = p.ws[(int64_t)n * kb + c];
+  }
 }
 
 template <int MODE>
 __global__ __launch_bounds__(NTHREADS) void qup_fwd_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-  run_tile<MODE>(p, lds);
-}
+  constexpr bool MX = Tile<MODE>::MX;
+  constexpr int KPS = Tile<MODE>::KPS;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING + (MX ? 2 * MAX_SCALE_BYTES : 0)];
+  uint8_t* xsc = lds + RING;
+  uint8_t* wsc = xsc + MAX_SCALE_BYTES;
 
-int grid_of(const FwdParams& p) {
-  const int64_t tiles_t = (p.T + TILE_T - 1) / TILE_T;
-  const int64_t tiles_n = (p.N + TILE_N - 1) / TILE_N;
-  return (int)(tiles_t * tiles_n);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave >> 1;  // which 128-row half of the N tile
+  const int wt = wave & 1;   // which 128-token half of the token tile
+  const int half = lane >> 5;
+  const int arow0 = wn * 128 + (lane & 31);
+  const int brow0 = wt * 128 + (lane & 31);
+
+  const TileGrid grid{(int)((p.T + TILE_T - 1) / TILE_T), (p.N + TILE_N - 1) / TILE_N, 0};
+  const TileGrid g{grid.tiles_t, grid.tiles_n, grid.tiles_t * grid.tiles_n};
+  const int row_bytes = MX ? p.K : 2 * p.K;
+  const int nk = p.K / KPS;
+  const int kblocks = p.K / 32;
+  const uint8_t* xb = static_cast<const uint8_t*>(p.x);
+  const uint8_t* wb = static_cast<const uint8_t*>(p.w);
+  const uint32_t ring = lds_u32(lds);
+  const TokenMap tm{p.fmt, p.B, p.S, p.cu, p.nseq};
+
+  int u = blockIdx.x;
+  if (u >= g.total) return;
+  int tt, tn;
+  tile_coords(g, u, tt, tn);
+  int64_t t0 = (int64_t)tt * TILE_T;
+  int n0 = tn * TILE_N;
+  DmaPlan dp = dma_plan(p, t0, n0, wave, lane, row_bytes);
+  if (MX) {
+    load_tile_scales(p, t0, n0, xsc, wsc, tid);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue_stage(dp, xb, wb, s, nk, s, ring, wave);
+
+  for (;;) {
+    f32x16_t acc[WBLK_N][WBLK_T];
+#pragma unroll
+    for (int i = 0; i < WBLK_N; ++i)
+#pragma unroll
+      for (int j = 0; j < WBLK_T; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    for (int kt = 0; kt < nk; ++kt) {
+      vm_wait<(STAGES - 2) * LPS>();
+      barrier();
+      // Always issue (past the last stage the source clamps to it) so every
+      // iteration has the same number of loads in flight; slot
+      // (kt + STAGES - 1) % STAGES was read in iteration kt - 1 and every
+      // wave has passed the barrier since.
+      issue_stage(dp, xb, wb, kt + STAGES - 1, nk, kt + STAGES - 1, ring, wave);
+      mma_stage<MODE>(acc, lds + (kt % STAGES) * SB, xsc, wsc, kblocks, kt, arow0, brow0, half);
+    }
+
+    // Next tile of this workgroup: start its first stages before the
+    // epilogue of the current one.
+    const int un = u + gridDim.x;
+    const bool more = un < g.total;
+    const int64_t t0c = t0;
+    const int n0c = n0;
+    vm_wait<0>();
+    barrier();
+    if (more) {
+      tile_coords(g, un, tt, tn);
+      t0 = (int64_t)tt * TILE_T;
+      n0 = tn * TILE_N;
+      dp = dma_plan(p, t0, n0, wave, lane, row_bytes);
+#pragma unroll
+      for (int s = 0; s < STAGES - 1; ++s) issue_stage(dp, xb, wb, s, nk, s, ring, wave);
+    }
+    epilogue_all(p, tm, acc, n0c + wn * 128, t0c + wt * 128 + (lane & 31), lane,
+                 std::make_integer_sequence<int, WBLK_N * WBLK_T>{});
+    if (!more) break;
+    u = un;
+    if (MX) {
+      // the scale area is only read inside the main loop: every wave passed
+      // the barrier above after its last read
+      load_tile_scales(p, t0, n0, xsc, wsc, tid);
+      __syncthreads();
+    }
+  }
 }
 
 }  // namespace
 
+int fwd_grid(const FwdParams& p, int num_cus) {
+  const int64_t tiles = ((p.T + TILE_T - 1) / TILE_T) * ((p.N + TILE_N - 1) / TILE_N);
+  int64_t g = num_cus;
+  if (g % 8) g -= g % 8;
+  if (g < 8) g = 8;
+  return (int)(tiles < g ? tiles : g);
+}
+
+bool fwd_scales_fit(int K) { return TILE_T * (K / 32) <= MAX_SCALE_BYTES; }
+
 hipError_t launch_qup_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(qup_fwd_kernel<MODE_BF16>, dim3(grid_of(p)), dim3(NTHREADS), 0, stream, p);
+  hipLaunchKernelGGL(qup_fwd_kernel<MODE_BF16>, dim3(fwd_grid(p, device_cu_count())), dim3(NTHREADS), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_qup_fwd_mx(const FwdParams& p, hipStream_t stream) {
+  const dim3 grid(fwd_grid(p, device_cu_count()));
   if (p.mx_fp8_mfma)
-    hipLaunchKernelGGL(qup_fwd_kernel<MODE_MX_FP8>, dim3(grid_of(p)), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(qup_fwd_kernel<MODE_MX_FP8>, grid, dim3(NTHREADS), 0, stream, p);
   else
-    hipLaunchKernelGGL(qup_fwd_kernel<MODE_MX_EXACT>, dim3(grid_of(p)), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(qup_fwd_kernel<MODE_MX_EXACT>, grid, dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
