@@ -9,22 +9,25 @@
 // corrupting upstream tensor in-place" (the rotation is out of place: the
 // accumulator is rotated in registers, no intermediate q exists).
 //
-// Work decomposition (one 256-thread workgroup per CU, persistent):
-//   * tile = 256 tokens x 256 rows of N; 4 waves in 2 x 2, each wave owns
-//     128 rows x 128 tokens = 4 x 4 blocks of the 32x32 MFMA, 256 fp32
-//     accumulators per lane. The MFMA row axis is N (W is the A operand), so
+// Work decomposition (two independent 256-thread workgroups per CU, persistent,
+// so each SIMD runs one wave of each: one workgroup's barriers, LDS round trips
+// and epilogue are covered by the other's MFMAs):
+//   * tile = 128 tokens x 192 rows of N (one DeepSeek-V3 head); each of the 4
+//     waves owns 32 tokens x all 192 rows = 6 blocks of the 32x32 MFMA, 96
+//     fp32 accumulators per lane, so a lane pair holds a token's whole head. The MFMA row axis is N (W is the A operand), so
 //     a lane holds runs of 4 consecutive head-dim elements of one token:
 //     RoPE pairs are lane-local and a 32-element scale block is split
 //     between lanes l and l^32 (one xor-shuffle for its amax).
-//   * K streams through a 3-slot LDS ring of 64-byte row slices (32 bf16 or
-//     64 E4M3 K-values per row per stage), filled by direct global->LDS DMA
-//     (global_load_lds_dwordx4) issued two stages ahead; each wave counts
+//   * K streams through an LDS ring (4 slots for bf16, 3 for E4M3) of 64-byte
+//     row slices (32 bf16 or 64 E4M3 K-values per row per stage), filled by
+//     direct global->LDS DMA (global_load_lds_dwordx4) issued STAGES-1
+//     stages ahead; each wave counts
 //     its own outstanding DMA with s_waitcnt vmcnt and one s_barrier per
 //     stage publishes the slot. The main loop issues no other vector-memory
 //     instruction, so the counts are exact.
 //   * After the last stage of a tile, the first stages of the workgroup's
 //     next tile are put in flight before the epilogue runs.
-//   * Tiles are ordered so that the 32 workgroups resident on one XCD share
+//   * Tiles are ordered so that the 64 workgroups resident on one XCD share
 //     W and X slices in that XCD's L2.
 #include <utility>
 
@@ -34,20 +37,24 @@
 namespace mla {
 namespace {
 
-constexpr int TILE_T = 256;
-constexpr int TILE_N = 256;
+constexpr int TILE_T = 128;
+constexpr int TILE_N = 192;                // one DeepSeek-V3 head (D = 192)
 constexpr int NTHREADS = 256;
 constexpr int ROWB = 64;                  // bytes of one tile row per stage
-constexpr int XSB = TILE_T * ROWB;        // X part of a stage (16 KB)
-constexpr int WSB = TILE_N * ROWB;        // W part of a stage (16 KB)
-constexpr int SB = XSB + WSB;             // one ring slot (32 KB)
-constexpr int STAGES = 3;
-constexpr int RING = SB * STAGES;         // 96 KB
-constexpr int LQ = TILE_T / 64;           // DMA loads per wave per operand per stage
-constexpr int LPS = 2 * LQ;               // DMA loads per wave per stage
-constexpr int WBLK_N = 4;                 // 32-row blocks per wave
-constexpr int WBLK_T = 4;                 // 32-token blocks per wave
-constexpr int MAX_SCALE_BYTES = 16 * 1024;  // LDS for the MXFP8 operand scales of a tile
+constexpr int XSB = TILE_T * ROWB;        // X part of a stage (8 KB)
+constexpr int WSB = TILE_N * ROWB;        // W part of a stage (12 KB)
+constexpr int SB = XSB + WSB;             // one ring slot (28 KB)
+constexpr int STAGES_BF16 = 4;            // ring slots: 80 KB per workgroup
+constexpr int STAGES_MX = 3;              // 60 KB + 20 KB of operand scales
+constexpr int LQX = XSB / 1024 / 4;       // X DMA loads per wave per stage (1 KB each)
+constexpr int LQW = WSB / 1024 / 4;       // W DMA loads per wave per stage
+constexpr int LPS = LQX + LQW;            // DMA loads per wave per stage
+constexpr int WBLK_N = TILE_N / 32;       // 32-row blocks per wave (all rows of the tile)
+constexpr int WBLK_T = 1;                 // 32-token blocks per wave (32 tokens)
+constexpr int WG_PER_CU = 2;              // two independent workgroups per CU
+constexpr int MAX_KBLOCKS = 64;           // MXFP8: K <= 2048 (operand scales of a tile live in LDS)
+constexpr int XSC_BYTES = TILE_T * MAX_KBLOCKS;
+constexpr int WSC_BYTES = TILE_N * MAX_KBLOCKS;
 
 // Chunk swizzle of a 64-byte row (four 16-byte chunks): chunk c of row r is
 // stored at c ^ ((r >> 2) & 3), so that the 16 lanes of a fragment read that
@@ -102,8 +109,11 @@ __device__ __forceinline__ TokInfo tok_info(const FwdParams& p, const TokenMap& 
   return ti;
 }
 
-__device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokInfo& ti, const f32x16_t& acc,
-                                               int n_blk, int lane) {
+// One 32 (n) x 32 (token) block: bias, rotation, quantization, store.
+// Returns the block's E8M0 scale byte (MXFP8 output), which the caller
+// stores; `store_scale` makes this function store it itself instead.
+__device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const TokInfo& ti, const f32x16_t& acc,
+                                                   int n_blk, int lane, bool store_scale) {
   const int half = lane >> 5;
   const int h = n_blk / p.D;
   const int d_blk = n_blk - h * p.D;
@@ -122,29 +132,41 @@ __device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokInfo
   if (d_blk + 32 > p.d_nope && p.d_rope > 0) {
     const bool pos_ok = ti.ok && ti.pos >= 0 && ti.pos < p.rope_rows;
     const int64_t trow = (int64_t)(pos_ok ? ti.pos : 0) * p.rope_pairs;
+    // rows 4g + {0,1} and 4g + {2,3} of this lane are pairs i, i+1 of the
+    // table: one 8-byte load each when they are 8-byte aligned
+    const bool vec = ((p.d_nope | p.rope_pairs) & 1) == 0 && (p.d_nope & 3) == 0;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const int d = d_blk + 8 * (r >> 2) + 4 * half + (r & 3);
+    for (int g = 0; g < 4; ++g) {
+      const int d = d_blk + 8 * g + 4 * half;
       if (d >= p.d_nope) {
         const int i = (d - p.d_nope) >> 1;
-        float c = p.cos[trow + i];
-        float sn = p.sin[trow + i];
-        if (!pos_ok) c = sn = __builtin_nanf("");
-        const float a = v[r], bb = v[r + 1];
-        v[r] = a * c - bb * sn;
-        v[r + 1] = a * sn + bb * c;
+        float c0, c1, s0, s1;
+        if (vec) {
+          const float2 cc = *reinterpret_cast<const float2*>(p.cos + trow + i);
+          const float2 ss = *reinterpret_cast<const float2*>(p.sin + trow + i);
+          c0 = cc.x; c1 = cc.y; s0 = ss.x; s1 = ss.y;
+        } else {
+          c0 = p.cos[trow + i]; c1 = p.cos[trow + i + 1];
+          s0 = p.sin[trow + i]; s1 = p.sin[trow + i + 1];
+        }
+        if (!pos_ok) c0 = c1 = s0 = s1 = __builtin_nanf("");
+        const float a0 = v[4 * g], b0 = v[4 * g + 1], a1 = v[4 * g + 2], b1 = v[4 * g + 3];
+        v[4 * g] = a0 * c0 - b0 * s0;
+        v[4 * g + 1] = a0 * s0 + b0 * c0;
+        v[4 * g + 2] = a1 * c1 - b1 * s1;
+        v[4 * g + 3] = a1 * s1 + b1 * c1;
       }
     }
   }
 
   const int64_t row = ti.row + (int64_t)h * p.S;  // BHSD (b, h, s)
+  uint32_t sc = 0;
   if (p.out_mx) {
     uint32_t m = 0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) m = max(m, abs_bits(v[r]));
     m = max(m, (uint32_t)__shfl_xor((int)m, 32));
     uint32_t P[4];
-    uint32_t sc;
     if (m >= 0x7F800000u) {
       P[0] = P[1] = P[2] = P[3] = 0x7F7F7F7Fu;
       sc = 0xFF;
@@ -164,7 +186,7 @@ __device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokInfo
     if (ti.ok) {
       uint8_t* dst = static_cast<uint8_t*>(p.out) + row * p.D + d_blk + 16 * half;
       *reinterpret_cast<u32x4_t*>(dst) = o;
-      if (half == 0) p.out_scales[row * (p.D / 32) + d_blk / 32] = (uint8_t)sc;
+      if (store_scale && half == 0) p.out_scales[row * (p.D / 32) + d_blk / 32] = (uint8_t)sc;
     }
   } else {
     uint32_t P[8];
@@ -192,31 +214,53 @@ __device__ __forceinline__ void epilogue_block(const FwdParams& p, const TokInfo
       reinterpret_cast<u32x4_t*>(dst)[1] = o1;
     }
   }
+  return sc;
 }
 
 // The epilogue body is too large for the loop unroller, and a runtime index
-// into the accumulator array would place it in scratch memory; a fold over a
-// compile-time index sequence keeps every accumulator access constant.
-template <int I>
-__device__ __forceinline__ void epilogue_one(const FwdParams& p, const TokInfo (&ti)[WBLK_T],
-                                             const f32x16_t (&acc)[WBLK_N][WBLK_T], int n_wave, int lane) {
-  constexpr int nb = I / WBLK_T;
-  constexpr int tb = I % WBLK_T;
-  const int n_blk = n_wave + 32 * nb;
+// into the accumulator array would place it in scratch memory; folds over
+// compile-time index sequences keep every accumulator access constant.
+template <int TB, int NB>
+__device__ __forceinline__ void epilogue_one(const FwdParams& p, const TokInfo& ti,
+                                             const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int lane,
+                                             bool packed, uint32_t (&sc)[WBLK_N]) {
+  const int n_blk = n0 + 32 * NB;
   // one block at a time: interleaving blocks would hold several blocks'
-  // temporaries live next to the 256 accumulators
+  // temporaries live next to the accumulators
   __builtin_amdgcn_sched_barrier(0);
-  if (n_blk < p.N) epilogue_block(p, ti[tb], acc[nb][tb], n_blk, lane);
+  sc[NB] = n_blk < p.N ? epilogue_block(p, ti, acc[NB][TB], n_blk, lane, !packed) : 0u;
 }
 
-template <int... Is>
-__device__ __forceinline__ void epilogue_all(const FwdParams& p, const TokenMap& tm,
-                                             const f32x16_t (&acc)[WBLK_N][WBLK_T], int n_wave,
-                                             int64_t t_lane, int lane, std::integer_sequence<int, Is...>) {
-  TokInfo ti[WBLK_T];
+template <int TB, int... NBs>
+__device__ __forceinline__ void epilogue_tok(const FwdParams& p, const TokenMap& tm,
+                                             const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int64_t t_lane,
+                                             int lane, std::integer_sequence<int, NBs...>) {
+  const TokInfo ti = tok_info(p, tm, t_lane + 32 * TB);
+  // When the tile is exactly one head, the head's D/32 scale bytes of this
+  // token are contiguous: store them as 16-bit pairs, right after the token
+  // row's codes, instead of one byte per block.
+  const bool packed = p.out_mx && p.D == TILE_N;
+  uint32_t sc[WBLK_N];
+  (epilogue_one<TB, NBs>(p, ti, acc, n0, lane, packed, sc), ...);
+  if (packed && ti.ok && lane < 32) {
+    const int64_t row = ti.row + (int64_t)(n0 / p.D) * p.S;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(p.out_scales + row * (TILE_N / 32));
 #pragma unroll
-  for (int tb = 0; tb < WBLK_T; ++tb) ti[tb] = tok_info(p, tm, t_lane + 32 * tb);
-  (epilogue_one<Is>(p, ti, acc, n_wave, lane), ...);
+    for (int k = 0; k < WBLK_N / 2; ++k) dst[k] = (uint16_t)(sc[2 * k] | (sc[2 * k + 1] << 8));
+  }
+}
+
+template <int... TBs>
+__device__ __forceinline__ void epilogue_all(const FwdParams& p, const TokenMap& tm,
+                                             const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int64_t t_lane,
+                                             int lane, std::integer_sequence<int, TBs...>) {
+  (epilogue_tok<TBs>(p, tm, acc, n0, t_lane, lane, std::make_integer_sequence<int, WBLK_N>{}), ...);
+}
+
+__device__ __forceinline__ void epilogue_tile(const FwdParams& p, const TokenMap& tm,
+                                              const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int64_t t_lane,
+                                              int lane) {
+  epilogue_all(p, tm, acc, n0, t_lane, lane, std::make_integer_sequence<int, WBLK_T>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -228,13 +272,20 @@ struct TileGrid {
 
 // Tile u -> (token tile, n tile). Workgroup g runs on XCD g % 8 and takes
 // tiles g, g + G, g + 2G, ... (G a multiple of 8), so every tile of one XCD
-// has u % 8 == xcd. Each XCD owns a contiguous run of the n-major tile order;
-// in one round its 32 resident workgroups cover 16 token tiles of 2 n tiles.
+// has u % 8 == xcd; v = xcd * (total / 8) + u / 8 gives each XCD a contiguous
+// run of v. v is then decoded in groups of 4 token tiles: 32 consecutive v
+// (one round of the XCD's 32 resident workgroups) cover 4 token tiles x 8 n
+// tiles, whose K slices the XCD's L2 serves to all 32 at once.
+constexpr int GROUP_T = 8;
 __device__ __forceinline__ void tile_coords(const TileGrid& g, int u, int& tt, int& tn) {
   int v = u;
   if ((g.total & 7) == 0) v = (u & 7) * (g.total >> 3) + (u >> 3);
-  tt = v % g.tiles_t;
-  tn = v / g.tiles_t;
+  const int per_group = GROUP_T * g.tiles_n;
+  const int first_t = (v / per_group) * GROUP_T;
+  const int rows = min(g.tiles_t - first_t, GROUP_T);
+  const int w = v % per_group;
+  tt = first_t + w % rows;
+  tn = w / rows;
 }
 
 enum { MODE_BF16 = 0, MODE_MX_EXACT = 1, MODE_MX_FP8 = 2 };
@@ -250,8 +301,8 @@ struct Tile {
 // that partial tiles never read out of bounds; clamped rows only feed
 // accumulators the epilogue discards).
 struct DmaPlan {
-  uint32_t xo[LQ];
-  uint32_t wo[LQ];
+  uint32_t xo[LQX];
+  uint32_t wo[LQW];
 };
 
 __device__ __forceinline__ DmaPlan dma_plan(const FwdParams& p, int64_t t0, int n0, int wave, int lane,
@@ -260,13 +311,15 @@ __device__ __forceinline__ DmaPlan dma_plan(const FwdParams& p, int64_t t0, int 
   const int lr = lane >> 2;
   const int c = (lane & 3) ^ swz(lr);
 #pragma unroll
-  for (int q = 0; q < LQ; ++q) {
-    const int r = 16 * (4 * q + wave) + lr;
-    int64_t t = t0 + r;
+  for (int q = 0; q < LQX; ++q) {
+    int64_t t = t0 + 16 * (4 * q + wave) + lr;
     if (t >= p.T) t = p.T - 1;
-    int n = n0 + r;
-    if (n >= p.N) n = p.N - 1;
     d.xo[q] = (uint32_t)(t * row_bytes + c * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < LQW; ++q) {
+    int n = n0 + 16 * (4 * q + wave) + lr;
+    if (n >= p.N) n = p.N - 1;
     d.wo[q] = (uint32_t)((int64_t)n * row_bytes + c * 16);
   }
   return d;
@@ -274,14 +327,15 @@ __device__ __forceinline__ DmaPlan dma_plan(const FwdParams& p, int64_t t0, int 
 
 // Stage `kt` of the tile (K slice kt, clamped to the last one) into ring
 // slot `slot_kt % STAGES`.
+template <int STAGES>
 __device__ __forceinline__ void issue_stage(const DmaPlan& d, const uint8_t* xb, const uint8_t* wb,
                                             int kt, int nk, int slot_kt, uint32_t ring, int wave) {
   const uint32_t slot = ring + (uint32_t)(slot_kt % STAGES) * SB;
   const int64_t kb = (int64_t)(kt < nk ? kt : nk - 1) * ROWB;
 #pragma unroll
-  for (int q = 0; q < LQ; ++q) dma16(xb + kb, d.xo[q], slot + (4 * q + wave) * 1024);
+  for (int q = 0; q < LQX; ++q) dma16(xb + kb, d.xo[q], slot + (4 * q + wave) * 1024);
 #pragma unroll
-  for (int q = 0; q < LQ; ++q) dma16(wb + kb, d.wo[q], slot + XSB + (4 * q + wave) * 1024);
+  for (int q = 0; q < LQW; ++q) dma16(wb + kb, d.wo[q], slot + XSB + (4 * q + wave) * 1024);
 }
 
 // Four E4M3 codes -> four bf16 (two dwords), each times 2^(scale - 127).
@@ -296,14 +350,14 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(s ? (s << 23) : 0x00400000u);
 }
 
-__device__ __forceinline__ bf16x8_t frag_mx_exact(const uint8_t* rowp, int j, int half, int r,
-                                                  float scale) {
-  // 8 codes: K-values 16 j + 8 half .. +7 of this row slice (chunk j)
-  const u32x2_t c = *reinterpret_cast<const u32x2_t*>(rowp + ((j ^ swz(r)) << 4) + 8 * half);
-  const u32x2_t lo = cvt4(c[0], scale);
-  const u32x2_t hi = cvt4(c[1], scale);
-  const u32x4_t v = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(bf16x8_t, v);
+__device__ __forceinline__ void frag_mx_exact(const uint8_t* rowp, int c, int r, float scale, bf16x8_t& f0,
+                                              bf16x8_t& f1) {
+  // 16 codes of chunk c of this row slice -> two bf16x8 fragments
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rowp + ((c ^ swz(r)) << 4));
+  const u32x2_t q0 = cvt4(v[0], scale), q1 = cvt4(v[1], scale);
+  const u32x2_t q2 = cvt4(v[2], scale), q3 = cvt4(v[3], scale);
+  f0 = __builtin_bit_cast(bf16x8_t, u32x4_t{q0[0], q0[1], q1[0], q1[1]});
+  f1 = __builtin_bit_cast(bf16x8_t, u32x4_t{q2[0], q2[1], q3[0], q3[1]});
 }
 
 template <int MODE>
@@ -311,43 +365,56 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
                                           const uint8_t* xsc, const uint8_t* wsc, int kblocks, int kt,
                                           int arow0, int brow0, int half) {
   if (MODE == MODE_BF16) {
+    // all fragments of both k16 steps first, so the second step's LDS reads
+    // are in flight while the first step's MFMAs run
+    bf16x8_t a[2][WBLK_N], b[2][WBLK_T];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {  // two k16 steps per 32-value slice
-      bf16x8_t a[WBLK_N], b[WBLK_T];
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int nb = 0; nb < WBLK_N; ++nb)
-        a[nb] = *reinterpret_cast<const bf16x8_t*>(cur + XSB + roff(arow0 + 32 * nb, 2 * j + half));
+        a[j][nb] = *reinterpret_cast<const bf16x8_t*>(cur + XSB + roff(arow0 + 32 * nb, 2 * j + half));
 #pragma unroll
       for (int tb = 0; tb < WBLK_T; ++tb)
-        b[tb] = *reinterpret_cast<const bf16x8_t*>(cur + roff(brow0 + 32 * tb, 2 * j + half));
-#pragma unroll
-      for (int nb = 0; nb < WBLK_N; ++nb)
-#pragma unroll
-        for (int tb = 0; tb < WBLK_T; ++tb)
-          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[tb], acc[nb][tb], 0, 0, 0);
+        b[j][tb] = *reinterpret_cast<const bf16x8_t*>(cur + roff(brow0 + 32 * tb, 2 * j + half));
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int tb = 0; tb < WBLK_T; ++tb)
+#pragma unroll
+        for (int nb = 0; nb < WBLK_N; ++nb)
+          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][nb], b[j][tb], acc[nb][tb], 0, 0, 0);
   } else if (MODE == MODE_MX_EXACT) {
     // E4M3 expanded exactly to bf16 (code * 2^(scale-127)) per fragment; the
-    // bf16 MFMA then multiplies exactly and accumulates in fp32.
+    // bf16 MFMA then multiplies exactly and accumulates in fp32. K is walked
+    // in a permuted but identical order for both operands: for K-block jb of
+    // the slice, lane half h reads the whole 16-byte chunk 2 jb + h, whose
+    // first and last 8 codes feed two k16 steps.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {  // four k16 steps per 64-value slice
-      const int kblk = 2 * kt + (j >> 1);
-      bf16x8_t a[WBLK_N], b[WBLK_T];
+    for (int jb = 0; jb < 2; ++jb) {
+      const int kblk = 2 * kt + jb;
+      const int c = 2 * jb + half;
+      bf16x8_t a0[WBLK_N], a1[WBLK_N], b0[WBLK_T], b1[WBLK_T];
 #pragma unroll
       for (int nb = 0; nb < WBLK_N; ++nb) {
         const int r = arow0 + 32 * nb;
-        a[nb] = frag_mx_exact(cur + XSB + r * ROWB, j, half, r, e8m0_to_f32(wsc[r * kblocks + kblk]));
+        frag_mx_exact(cur + XSB + r * ROWB, c, r, e8m0_to_f32(wsc[kblk * TILE_N + r]), a0[nb], a1[nb]);
       }
 #pragma unroll
       for (int tb = 0; tb < WBLK_T; ++tb) {
         const int r = brow0 + 32 * tb;
-        b[tb] = frag_mx_exact(cur + r * ROWB, j, half, r, e8m0_to_f32(xsc[r * kblocks + kblk]));
+        frag_mx_exact(cur + r * ROWB, c, r, e8m0_to_f32(xsc[kblk * TILE_T + r]), b0[tb], b1[tb]);
       }
 #pragma unroll
       for (int nb = 0; nb < WBLK_N; ++nb)
 #pragma unroll
         for (int tb = 0; tb < WBLK_T; ++tb)
-          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], b[tb], acc[nb][tb], 0, 0, 0);
+          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[nb], b0[tb], acc[nb][tb], 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < WBLK_N; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < WBLK_T; ++tb)
+          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[nb], b1[tb], acc[nb][tb], 0, 0, 0);
     }
   } else {
     // Scaled FP8 32x32x64: lane (row, half) holds 16 bytes of K-block 0
@@ -364,7 +431,7 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
       const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + XSB + roff(r, 2 + half));
       a[nb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      sa[nb] = wsc[r * kblocks + kblk];
+      sa[nb] = wsc[kblk * TILE_N + r];
     }
 #pragma unroll
     for (int tb = 0; tb < WBLK_T; ++tb) {
@@ -373,7 +440,7 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
       const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + roff(r, 2 + half));
       b[tb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      sb[tb] = xsc[r * kblocks + kblk];
+      sb[tb] = xsc[kblk * TILE_T + r];
     }
 #pragma unroll
     for (int nb = 0; nb < WBLK_N; ++nb)
@@ -384,19 +451,21 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
   }
 }
 
-// MXFP8 operand scales of a tile (all K blocks of its 256 X rows and 256 W
-// rows) copied into LDS with ordinary loads, before the main loop.
+// MXFP8 operand scales of a tile (all K blocks of its X and W rows) copied
+// into LDS with ordinary loads before the main loop, transposed to
+// [K block][row] so the 32 rows a wave reads are consecutive bytes.
 __device__ __forceinline__ void load_tile_scales(const FwdParams& p, int64_t t0, int n0, uint8_t* xsc,
                                                  uint8_t* wsc, int tid) {
   const int kb = p.K / 32;
+  // consecutive threads take consecutive rows: consecutive LDS bytes
   for (int e = tid; e < TILE_T * kb; e += NTHREADS) {
-    const int r = e / kb, c = e - r * kb;
+    const int c = e / TILE_T, r = e - c * TILE_T;
     int64_t t = t0 + r;
     if (t >= p.T) t = p.T - 1;
     xsc[e] = p.xs[t * kb + c];
   }
   for (int e = tid; e < TILE_N * kb; e += NTHREADS) {
-    const int r = e / kb, c = e - r * kb;
+    const int c = e / TILE_N, r = e - c * TILE_N;
     int n = n0 + r;
     if (n >= p.N) n = p.N - 1;
     wsc[e] = p.ws[(int64_t)n * kb + c];
@@ -404,21 +473,22 @@ __device__ __forceinline__ void load_tile_scales(const FwdParams& p, int64_t t0,
 }
 
 template <int MODE>
-__global__ __launch_bounds__(NTHREADS) void qup_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(WG_PER_CU, WG_PER_CU)))
+void qup_fwd_kernel(FwdParams p) {
   constexpr bool MX = Tile<MODE>::MX;
   constexpr int KPS = Tile<MODE>::KPS;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING + (MX ? 2 * MAX_SCALE_BYTES : 0)];
+  constexpr int STAGES = MX ? STAGES_MX : STAGES_BF16;
+  constexpr int RING = SB * STAGES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING + (MX ? XSC_BYTES + WSC_BYTES : 0)];
   uint8_t* xsc = lds + RING;
-  uint8_t* wsc = xsc + MAX_SCALE_BYTES;
+  uint8_t* wsc = xsc + XSC_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave >> 1;  // which 128-row half of the N tile
-  const int wt = wave & 1;   // which 128-token half of the token tile
   const int half = lane >> 5;
-  const int arow0 = wn * 128 + (lane & 31);
-  const int brow0 = wt * 128 + (lane & 31);
+  const int arow0 = lane & 31;               // every wave covers all TILE_N rows
+  const int brow0 = 32 * wave + (lane & 31);  // and 32 of the tile's tokens
 
   const TileGrid grid{(int)((p.T + TILE_T - 1) / TILE_T), (p.N + TILE_N - 1) / TILE_N, 0};
   const TileGrid g{grid.tiles_t, grid.tiles_n, grid.tiles_t * grid.tiles_n};
@@ -442,7 +512,7 @@ __global__ __launch_bounds__(NTHREADS) void qup_fwd_kernel(FwdParams p) {
     __syncthreads();
   }
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue_stage(dp, xb, wb, s, nk, s, ring, wave);
+  for (int s = 0; s < STAGES - 1; ++s) issue_stage<STAGES>(dp, xb, wb, s, nk, s, ring, wave);
 
   for (;;) {
     f32x16_t acc[WBLK_N][WBLK_T];
@@ -460,7 +530,7 @@ __global__ __launch_bounds__(NTHREADS) void qup_fwd_kernel(FwdParams p) {
       // iteration has the same number of loads in flight; slot
       // (kt + STAGES - 1) % STAGES was read in iteration kt - 1 and every
       // wave has passed the barrier since.
-      issue_stage(dp, xb, wb, kt + STAGES - 1, nk, kt + STAGES - 1, ring, wave);
+      issue_stage<STAGES>(dp, xb, wb, kt + STAGES - 1, nk, kt + STAGES - 1, ring, wave);
       mma_stage<MODE>(acc, lds + (kt % STAGES) * SB, xsc, wsc, kblocks, kt, arow0, brow0, half);
     }
 
@@ -478,10 +548,9 @@ __global__ __launch_bounds__(NTHREADS) void qup_fwd_kernel(FwdParams p) {
       n0 = tn * TILE_N;
       dp = dma_plan(p, t0, n0, wave, lane, row_bytes);
 #pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s) issue_stage(dp, xb, wb, s, nk, s, ring, wave);
+      for (int s = 0; s < STAGES - 1; ++s) issue_stage<STAGES>(dp, xb, wb, s, nk, s, ring, wave);
     }
-    epilogue_all(p, tm, acc, n0c + wn * 128, t0c + wt * 128 + (lane & 31), lane,
-                 std::make_integer_sequence<int, WBLK_N * WBLK_T>{});
+    epilogue_tile(p, tm, acc, n0c, t0c + 32 * wave + (lane & 31), lane);
     if (!more) break;
     u = un;
     if (MX) {
@@ -497,13 +566,13 @@ __global__ __launch_bounds__(NTHREADS) void qup_fwd_kernel(FwdParams p) {
 
 int fwd_grid(const FwdParams& p, int num_cus) {
   const int64_t tiles = ((p.T + TILE_T - 1) / TILE_T) * ((p.N + TILE_N - 1) / TILE_N);
-  int64_t g = num_cus;
+  int64_t g = (int64_t)num_cus * WG_PER_CU;
   if (g % 8) g -= g % 8;
   if (g < 8) g = 8;
   return (int)(tiles < g ? tiles : g);
 }
 
-bool fwd_scales_fit(int K) { return TILE_T * (K / 32) <= MAX_SCALE_BYTES; }
+bool fwd_scales_fit(int K) { return K / 32 <= MAX_KBLOCKS; }
 
 hipError_t launch_qup_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(qup_fwd_kernel<MODE_BF16>, dim3(fwd_grid(p, device_cu_count())), dim3(NTHREADS), 0,
