@@ -76,6 +76,37 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, flo
 }
 
 // ---------------------------------------------------------------------------
+// Direct global->LDS staging (gfx950 global_load_lds_dwordx4). Each kernel
+// that uses it issues no other vector-memory load inside its pipelined loop,
+// so a per-wave s_waitcnt vmcnt count names exactly which stages have landed.
+// ---------------------------------------------------------------------------
+
+// 16 bytes per lane: lane i of the wave writes LDS bytes [lds_addr + 16 i,
+// +16) from global sbase + voff (sbase wave-uniform).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the compiler's implied full memory wait.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+
+// ---------------------------------------------------------------------------
 // Token row -> (position, b, s). See the token-format comment in mla_qup.h.
 // ---------------------------------------------------------------------------
 struct TokenMap {

@@ -11,12 +11,10 @@
 //                     each rope pair; per-chunk fp32 column sums for db.
 //                     HBM-bound: 2 B read + 2 B written per element.
 //   db_reduce_kernel: db[n] = sum over chunks, in chunk order.
-//   gemm_kernel     : C[m, n] = sum_r A(m, r) B(n, r) on bf16 MFMA; an
-//                     operand whose reduction axis is strided in memory
-//                     (W for dX; dq_pre and X for dW) is loaded as 8 x 8
-//                     blocks and transposed in registers on its way into LDS.
-//   dX = dq_pre W       : A = dq_pre (r contiguous), B(k, r) = W[r, k]
-//   dW = dq_pre^T X     : A(n, t) = dq_pre[t, n], B(k, t) = X[t, k]
+//   bgemm_kernel    : dX = dq_pre W and dW = dq_pre^T X on bf16 MFMA; operands
+//                     reach LDS by DMA in memory order, and an operand whose
+//                     reduction axis is strided in memory is transposed by the
+//                     LDS transpose read (ds_read_b64_tr_b16).
 //   split_reduce_kernel: ordered sum of the dX reduction splits -> bf16.
 // No floating-point atomics anywhere: results are run-to-run deterministic.
 #include <algorithm>
@@ -136,206 +134,368 @@ __global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Generic bf16 MFMA GEMM, C[m, n] = sum_r A(m, r) * B(n, r).
-// Tile 256 (m) x 128 (n) x 64 (r), 4 waves in 2 x 2, wave tile 128 x 64.
-// MFMA rows are n, columns m (D = C^T block), so a lane owns 4 consecutive
-// n of one m: 8-byte (bf16) or 16-byte (fp32) stores.
+// Backward GEMMs on bf16 MFMA: out[j][i] = sum over r of P(i, r) Q(j, r).
+//   dX[t][k] : i = k, j = t, r = n; P(k, n) = W[n][k]       (n-rows in memory)
+//                                    Q(t, n) = dq_pre[t][n] (n contiguous)
+//   dW[n][k] : i = k, j = n, r = t; P(k, t) = X[t][k]       (t-rows in memory)
+//                                    Q(n, t) = dq_pre[t][n] (t-rows in memory)
+// P is always stored with its reduction index r as the row ("MN-major"); Q is
+// MN-major for dW and r-contiguous ("K-major") for dX.
+//
+// Persistent, two independent 256-thread workgroups per CU, tile 192 (i) x
+// 128 (j); waves 2 x 2, each 96 (i) x 64 (j) = 3 x 2 blocks of the 32x32x16
+// MFMA (P is the MFMA's row operand, so a lane holds 4 consecutive i of one j:
+// 16-byte fp32 or 8-byte bf16 stores). The reduction streams through a 4-slot
+// LDS ring of 32-value stages filled by direct global->LDS DMA in memory
+// order; nothing is transposed on the way in.
+//   * MN-major stage = 32 rows (r) x tile width, row pitch RP = 2 x width.
+//     Fragments come from ds_read_b64_tr_b16: within each 16-lane group, lane
+//     i receives element i%4 of the 8-byte row slices addressed by lanes
+//     4e + i/4 (e = 0..3). Lane 16g+s addresses row 8(g/2) + 4h + s/4 (h = 0,
+//     1 for the fragment's two reads), columns 16(g%2) + 4(s%4) .. +3 of its
+//     32-column block, which yields the MFMA operand layout (lane l: column
+//     l%32, reduction values 8(l/32) .. +7).
+//     A 32-lane half of such a read touches 4 consecutive rows x 64 bytes;
+//     64-byte segments are XOR-swizzled per row so those 4 land in distinct
+//     bank quarters: segment s ^ (r & 3) when RP is a multiple of 256 bytes,
+//     s ^ ((r >> 1) & 1) when RP = 128 mod 256.
+//   * K-major stage = tile rows x 64 bytes, 16-byte chunk c of row r stored at
+//     c ^ ((r >> 2) & 3), read with ds_read_b128 as in the forward.
+//   * A reduction tail (r past the end inside the last stage) is read from a
+//     clamped row and zeroed in both MN-major fragments before the MFMA. A
+//     K-major Q requires a reduction length that is a multiple of 32.
 // ---------------------------------------------------------------------------
-constexpr int G_BM = 256;
-constexpr int G_BN = 128;
-constexpr int G_ROW = 128;  // bytes per LDS row per stage (64 bf16 of r)
-constexpr int G_THREADS = 256;
-constexpr int G_A_STAGE = G_BM * G_ROW;
-constexpr int G_STAGE = (G_BM + G_BN) * G_ROW;  // 49152
-constexpr int G_LDS = 2 * G_STAGE;
+constexpr int BG_TI = 192;
+constexpr int BG_TJ = 128;
+constexpr int BG_KS = 32;
+constexpr int BG_THREADS = 256;
+constexpr int BG_STAGES = 4;
+constexpr int BG_WG_PER_CU = 2;
+constexpr int BG_RPP = BG_TI * 2;          // P row pitch (MN-major), bytes
+constexpr int BG_RPQ = BG_TJ * 2;          // Q row pitch when MN-major
+constexpr int BG_PB = BG_KS * BG_RPP;      // P part of a stage (12 KB)
+constexpr int BG_QB = BG_KS * BG_RPQ;      // Q part (8 KB, either layout)
+constexpr int BG_SB = BG_PB + BG_QB;
+constexpr int BG_LP = BG_PB / 4096;        // P DMA loads per wave per stage
+constexpr int BG_LQ = BG_QB / 4096;
+constexpr int BG_LPS = BG_LP + BG_LQ;
+constexpr int BG_BI = BG_TI / 64;          // 32-blocks of i per wave (2 waves along i)
+constexpr int BG_BJ = BG_TJ / 64;          // 32-blocks of j per wave
+static_assert(BG_PB % 4096 == 0 && BG_QB % 4096 == 0, "whole DMA rounds per stage");
 
-__device__ __forceinline__ int g_off(int r, int c) { return r * G_ROW + ((c ^ (r & 7)) << 4); }
+template <int RP>
+__device__ __forceinline__ int mn_swz(int r) {
+  if constexpr (RP % 256 == 0) return r & 3;
+  else if constexpr (RP % 256 == 128) return (r >> 1) & 1;
+  else return 0;  // RP = 64 or 192 mod 256: consecutive rows already differ
+}
 
-struct GemmArgs {
-  const uint16_t* a;
-  int64_t lda;  // element stride of A's slow axis
-  const uint16_t* b;
-  int64_t ldb;
-  int M, Nc;
-  int64_t R;
-  int64_t r_per_split;
-  void* c;      // [splits][M][Nc]
+struct BGemm {
+  const uint8_t* p;
+  int64_t ldp;        // bytes between P rows (consecutive r)
+  const uint8_t* q;
+  int64_t ldq;        // bytes between Q rows (r for MN-major, j for K-major)
+  int I, J;           // output columns / rows; I % 8 == 0
+  int64_t R;          // reduction length
+  int splits;         // reduction splits; split z covers stages [z*sps, (z+1)*sps)
+  int sps;
+  void* out;          // [splits][J][I] (fp32) or [J][I] (bf16)
   int out_f32;
 };
 
-// Operand staging for one stage: rows x 64 of the reduction axis.
-// K-major (reduction contiguous): rows*8 16-byte chunks, ROWS*8/256 per thread.
-// MN-major (rows contiguous): (rows/8) x 8 blocks of 8x8, one per thread.
-template <int ROWS, bool KMAJOR>
-struct OperandStage {
-  static constexpr int NCH = KMAJOR ? ROWS * 8 / G_THREADS : 8;
-  u32x4_t v[NCH];
+struct BgGrid {
+  int ti, tj, per, total;
 };
 
-template <int ROWS, bool KMAJOR>
-__device__ __forceinline__ void op_load(OperandStage<ROWS, KMAJOR>& st, const uint16_t* __restrict__ base,
-                                        int64_t ld, int row0, int rows_valid, int64_t r0, int64_t r_end,
-                                        int tid) {
-  if (KMAJOR) {
-    const int c = tid & 7;
-    const int64_t r = r0 + c * 8;
+__device__ __forceinline__ void bg_coords(const BgGrid& g, int u, int& z, int& ti, int& tj) {
+  int v = u;
+  if ((g.total & 7) == 0) v = (u & 7) * (g.total >> 3) + (u >> 3);  // one run of v per XCD
+  z = v / g.per;
+  const int w = v - z * g.per;
+  ti = w % g.ti;  // i fastest: the tiles sharing a Q slice run together
+  tj = w / g.ti;
+}
+
+// Per-lane DMA sources of one tile (independent of the stage).
+struct BgDma {
+  int pr[BG_LP];       // P: stage row
+  uint32_t pc[BG_LP];  // P: byte offset inside the row (tile column base included)
+  int qr[BG_LQ];       // Q MN-major: stage row; K-major: unused
+  uint32_t qc[BG_LQ];  // Q MN-major: byte offset in row; K-major: row offset + chunk
+};
+
+// Chunk e (16 bytes) of an MN-major stage of `COLS` columns: its stage row
+// and the byte offset of its source in that row, columns clamped into the
+// matrix (clamped chunks only feed discarded outputs).
+template <int COLS>
+__device__ __forceinline__ void mn_src(int e, int col0, int cols, int& row, uint32_t& off) {
+  constexpr int CPR = COLS / 8;
+  row = e / CPR;
+  const int cp = e - row * CPR;
+  int gc = 4 * ((cp >> 2) ^ mn_swz<COLS * 2>(row)) + (cp & 3);
+  const int last = (cols - col0) / 8 - 1;
+  if (gc > last) gc = last;
+  off = (uint32_t)((col0 + gc * 8) * 2);
+}
+
+template <bool QK>
+__device__ __forceinline__ BgDma bg_dma(const BGemm& g, int i0, int j0, int wave, int lane) {
+  BgDma d;
 #pragma unroll
-    for (int i = 0; i < st.NCH; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      if (row < rows_valid && r < r_end)
-        st.v[i] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)(row0 + row) * ld + r);
-      else
-        st.v[i] = u32x4_t{0, 0, 0, 0};
+  for (int q = 0; q < BG_LP; ++q) mn_src<BG_TI>((4 * q + wave) * 64 + lane, i0, g.I, d.pr[q], d.pc[q]);
+  if (QK) {
+#pragma unroll
+    for (int q = 0; q < BG_LQ; ++q) {
+      const int row = 16 * (4 * q + wave) + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      int j = j0 + row;
+      if (j >= g.J) j = g.J - 1;
+      d.qr[q] = 0;
+      d.qc[q] = (uint32_t)((int64_t)(j - j0) * g.ldq + c * 16);
     }
   } else {
-    constexpr int MBLK = ROWS / 8;
-    const int mb = tid % MBLK;
-    const int rb = tid / MBLK;
-    const bool active = rb < 8;
-    const int row = 8 * mb;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t r = r0 + 8 * rb + j;
-      if (active && row < rows_valid && r < r_end)
-        st.v[j] = *reinterpret_cast<const u32x4_t*>(base + r * ld + row0 + row);
-      else
-        st.v[j] = u32x4_t{0, 0, 0, 0};
-    }
+    for (int q = 0; q < BG_LQ; ++q) mn_src<BG_TJ>((4 * q + wave) * 64 + lane, j0, g.J, d.qr[q], d.qc[q]);
+  }
+  return d;
+}
+
+// Stage whose reduction rows start at rs (rows past rlim are clamped to it)
+// into the ring slot at LDS address `slot`.
+template <bool QK>
+__device__ __forceinline__ void bg_issue(const BGemm& g, const BgDma& d, const uint8_t* qtile, int64_t rs,
+                                         int rlim, uint32_t slot, int wave) {
+  const uint8_t* ps = g.p + rs * g.ldp;
+  const uint32_t ldp = (uint32_t)g.ldp;
+#pragma unroll
+  for (int q = 0; q < BG_LP; ++q)
+    dma16(ps, (uint32_t)min(d.pr[q], rlim) * ldp + d.pc[q], slot + (4 * q + wave) * 1024);
+  if (QK) {
+    const uint8_t* qs = qtile + rs * 2;
+#pragma unroll
+    for (int q = 0; q < BG_LQ; ++q) dma16(qs, d.qc[q], slot + BG_PB + (4 * q + wave) * 1024);
+  } else {
+    const uint8_t* qs = g.q + rs * g.ldq;
+    const uint32_t ldq = (uint32_t)g.ldq;
+#pragma unroll
+    for (int q = 0; q < BG_LQ; ++q)
+      dma16(qs, (uint32_t)min(d.qr[q], rlim) * ldq + d.qc[q], slot + BG_PB + (4 * q + wave) * 1024);
   }
 }
 
-template <int ROWS, bool KMAJOR>
-__device__ __forceinline__ void op_store(const OperandStage<ROWS, KMAJOR>& st, uint8_t* lds, int tid) {
-  if (KMAJOR) {
-    const int c = tid & 7;
-#pragma unroll
-    for (int i = 0; i < st.NCH; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      *reinterpret_cast<u32x4_t*>(lds + g_off(row, c)) = st.v[i];
-    }
-  } else {
-    constexpr int MBLK = ROWS / 8;
-    const int mb = tid % MBLK;
-    const int rb = tid / MBLK;
-    if (rb >= 8) return;
-    // st.v[j] holds 8 values of rows 8mb..8mb+7 at reduction index 8rb+j;
-    // out[i] gathers the 8 reduction values of row 8mb+i.
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int w = i >> 1;
-      uint32_t o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = st.v[2 * q][w];
-        const uint32_t hi = st.v[2 * q + 1][w];
-        o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-      }
-      *reinterpret_cast<u32x4_t*>(lds + g_off(8 * mb + i, rb)) = u32x4_t{o[0], o[1], o[2], o[3]};
-    }
-  }
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// One MFMA operand fragment (32 columns x 16 reduction values) of an MN-major
+// stage: two transpose reads, 4 rows apart.
+__device__ __forceinline__ bf16x8_t tr_frag(uint32_t addr, int rp) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)addr);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)(addr + 4 * rp));
+  const i16x4_t v0 = lo, v1 = hi;
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <bool A_KMAJOR, bool B_KMAJOR>
-__global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[G_LDS];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+// Zero the values of a fragment whose reduction index (kbase + e) >= rem.
+__device__ __forceinline__ bf16x8_t mask_tail(bf16x8_t f, int kbase, int rem) {
+  u32x4_t u = __builtin_bit_cast(u32x4_t, f);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = kbase + 2 * w < rem ? 0x0000FFFFu : 0u;
+    const uint32_t hi = kbase + 2 * w + 1 < rem ? 0xFFFF0000u : 0u;
+    u[w] &= lo | hi;
+  }
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// Lane-constant parts of the fragment addresses (bytes from the stage base).
+struct BgFrag {
+  uint32_t p[BG_BI];  // P block ib, row group of this lane, swizzled segment
+  uint32_t q[BG_BJ];  // Q block jb
+};
+
+template <bool QK>
+__device__ __forceinline__ BgFrag bg_frag(int wi, int wj, int lane) {
+  BgFrag f;
+  const int g = lane >> 4, s = lane & 15;
+  const int rsub = 8 * (g >> 1) + (s >> 2);         // row inside a 16-row step
+  const int cin = 32 * (g & 1) + 8 * (s & 3);        // byte inside the 64-byte segment
+#pragma unroll
+  for (int ib = 0; ib < BG_BI; ++ib)
+    f.p[ib] = rsub * BG_RPP + (((BG_BI * wi + ib) ^ mn_swz<BG_RPP>(rsub)) << 6) + cin;
+#pragma unroll
+  for (int jb = 0; jb < BG_BJ; ++jb) {
+    if (QK) {
+      const int row = 64 * wj + 32 * jb + (lane & 31);
+      f.q[jb] = BG_PB + row * 64;  // chunk added per step
+    } else {
+      f.q[jb] = BG_PB + rsub * BG_RPQ + (((BG_BJ * wj + jb) ^ mn_swz<BG_RPQ>(rsub)) << 6) + cin;
+    }
+  }
+  return f;
+}
+
+template <bool QK, bool TAIL>
+__device__ __forceinline__ void bg_mma(f32x16_t (&acc)[BG_BI][BG_BJ], uint32_t cur, const BgFrag& f, int lane,
+                                       int rem) {
   const int half = lane >> 5;
-
-  const int tiles_m = (g.M + G_BM - 1) / G_BM;
-  const int tiles_n = (g.Nc + G_BN - 1) / G_BN;
-  const int total = tiles_m * tiles_n;
-  int id = blockIdx.x;
-  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  const int tm = id % tiles_m;
-  const int tn = id / tiles_m;
-  const int m0 = tm * G_BM;
-  const int n0 = tn * G_BN;
-  const int64_t r_begin = (int64_t)blockIdx.z * g.r_per_split;
-  int64_t r_end = r_begin + g.r_per_split;
-  if (r_end > g.R) r_end = g.R;
-  const int nk = (int)((r_end - r_begin + 63) / 64);
-  const int m_valid = g.M - m0;
-  const int n_valid = g.Nc - n0;
-
-  f32x16_t acc[2][4];
+  bf16x8_t a[2][BG_BI], b[2][BG_BJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int js = 0; js < 2; ++js) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int ib = 0; ib < BG_BI; ++ib) a[js][ib] = tr_frag(cur + f.p[ib] + 16 * js * BG_RPP, BG_RPP);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  OperandStage<G_BM, A_KMAJOR> sa;
-  OperandStage<G_BN, B_KMAJOR> sb;
-  const uint16_t* abase = g.a;
-  op_load<G_BM, A_KMAJOR>(sa, abase, g.lda, m0, m_valid, r_begin, r_end, tid);
-  op_load<G_BN, B_KMAJOR>(sb, g.b, g.ldb, n0, n_valid, r_begin, r_end, tid);
-  op_store<G_BM, A_KMAJOR>(sa, lds, tid);
-  op_store<G_BN, B_KMAJOR>(sb, lds + G_A_STAGE, tid);
-  __syncthreads();
-
-  const int arow0 = wm * 128 + (lane & 31);  // m rows (MFMA columns)
-  const int brow0 = wn * 64 + (lane & 31);   // n rows (MFMA rows)
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int64_t rn = r_begin + (int64_t)(kt + 1) * 64;
-      op_load<G_BM, A_KMAJOR>(sa, abase, g.lda, m0, m_valid, rn, r_end, tid);
-      op_load<G_BN, B_KMAJOR>(sb, g.b, g.ldb, n0, n_valid, rn, r_end, tid);
+    for (int jb = 0; jb < BG_BJ; ++jb) {
+      if (QK) {
+        const int c = (2 * js + half) ^ (((lane & 31) >> 2) & 3);
+        b[js][jb] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+            (uintptr_t)(cur + f.q[jb] + (c << 4)));
+      } else {
+        b[js][jb] = tr_frag(cur + f.q[jb] + 16 * js * BG_RPQ, BG_RPQ);
+      }
     }
-    const uint8_t* cur = lds + (kt & 1) * G_STAGE;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ch = 2 * j + half;
-      bf16x8_t af[4], bfr[2];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        af[mb] = *reinterpret_cast<const bf16x8_t*>(cur + g_off(arow0 + 32 * mb, ch));
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        bfr[nb] = *reinterpret_cast<const bf16x8_t*>(cur + G_A_STAGE + g_off(brow0 + 32 * nb, ch));
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
-    }
-    if (more) {
-      uint8_t* nxt = lds + ((kt + 1) & 1) * G_STAGE;
-      op_store<G_BM, A_KMAJOR>(sa, nxt, tid);
-      op_store<G_BN, B_KMAJOR>(sb, nxt + G_A_STAGE, tid);
-    }
-    __syncthreads();
   }
+  if (TAIL) {
+#pragma unroll
+    for (int js = 0; js < 2; ++js) {
+      const int kb = 16 * js + 8 * half;
+#pragma unroll
+      for (int ib = 0; ib < BG_BI; ++ib) a[js][ib] = mask_tail(a[js][ib], kb, rem);
+      if (!QK) {
+#pragma unroll
+        for (int jb = 0; jb < BG_BJ; ++jb) b[js][jb] = mask_tail(b[js][jb], kb, rem);
+      }
+    }
+  }
+#pragma unroll
+  for (int js = 0; js < 2; ++js)
+#pragma unroll
+    for (int jb = 0; jb < BG_BJ; ++jb)
+#pragma unroll
+      for (int ib = 0; ib < BG_BI; ++ib)
+        acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[js][ib], b[js][jb], acc[ib][jb], 0, 0, 0);
+}
 
-  // acc[nb][mb] lane l, reg r: n = n0 + wn*64 + 32nb + 8(r/4) + 4half + r%4,
-  // m = m0 + wm*128 + 32mb + lane%32.
-  const int64_t split_off = (int64_t)blockIdx.z * g.M * g.Nc;
+// acc[ib][jb] lane l, register r: i = i0 + 96 wi + 32 ib + 8 (r/4) + 4 (l/32) + r%4,
+// j = j0 + 64 wj + 32 jb + l%32.
+__device__ __forceinline__ void bg_store(const BGemm& g, const f32x16_t (&acc)[BG_BI][BG_BJ], int z, int i0,
+                                         int j0, int wi, int wj, int lane) {
+  const int half = lane >> 5;
+  const int64_t zoff = (int64_t)z * g.J * g.I;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int jb = 0; jb < BG_BJ; ++jb) {
+    const int j = j0 + 64 * wj + 32 * jb + (lane & 31);
+    if (j >= g.J) continue;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 128 + 32 * mb + (lane & 31);
-      if (m >= g.M) continue;
+    for (int ib = 0; ib < BG_BI; ++ib) {
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        const int n = n0 + wn * 64 + 32 * nb + 8 * grp + 4 * half;
-        if (n >= g.Nc) continue;
-        const float v0 = acc[nb][mb][4 * grp + 0], v1 = acc[nb][mb][4 * grp + 1];
-        const float v2 = acc[nb][mb][4 * grp + 2], v3 = acc[nb][mb][4 * grp + 3];
-        const int64_t idx = split_off + (int64_t)m * g.Nc + n;
-        if (g.out_f32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(g.c) + idx) = make_float4(v0, v1, v2, v3);
-        } else {
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.c) + idx) =
+        const int i = i0 + 32 * (BG_BI * wi + ib) + 8 * grp + 4 * half;
+        if (i >= g.I) continue;
+        const float v0 = acc[ib][jb][4 * grp], v1 = acc[ib][jb][4 * grp + 1];
+        const float v2 = acc[ib][jb][4 * grp + 2], v3 = acc[ib][jb][4 * grp + 3];
+        const int64_t idx = zoff + (int64_t)j * g.I + i;
+        if (g.out_f32)
+          *reinterpret_cast<float4*>(static_cast<float*>(g.out) + idx) = make_float4(v0, v1, v2, v3);
+        else
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + idx) =
               make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-        }
       }
     }
+  }
+}
+
+template <bool QK>
+__global__ __launch_bounds__(BG_THREADS) __attribute__((amdgpu_waves_per_eu(BG_WG_PER_CU, BG_WG_PER_CU)))
+void bgemm_kernel(BGemm g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[BG_STAGES * BG_SB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = wave >> 1, wj = wave & 1;
+  const uint32_t ring = lds_u32(lds);
+
+  BgGrid gr;
+  gr.ti = (g.I + BG_TI - 1) / BG_TI;
+  gr.tj = (g.J + BG_TJ - 1) / BG_TJ;
+  gr.per = gr.ti * gr.tj;
+  gr.total = gr.per * g.splits;
+  const BgFrag fr = bg_frag<QK>(wi, wj, lane);
+
+  int u = blockIdx.x;
+  if (u >= gr.total) return;
+  int z, ti, tj;
+  bg_coords(gr, u, z, ti, tj);
+  int i0 = ti * BG_TI, j0 = tj * BG_TJ;
+  int64_t r0 = (int64_t)z * g.sps * BG_KS;
+  int64_t r1 = min(g.R, r0 + (int64_t)g.sps * BG_KS);
+  int nk = (int)((r1 - r0 + BG_KS - 1) / BG_KS);
+  BgDma dp = bg_dma<QK>(g, i0, j0, wave, lane);
+  const uint8_t* qt = g.q + (int64_t)j0 * g.ldq;  // K-major Q: the tile's first row
+
+  // stage kt of the current tile (clamped to the last one) into slot s
+  auto issue = [&](int kt, int slot_kt) {
+    const int k = kt < nk ? kt : nk - 1;
+    const int64_t rs = r0 + (int64_t)k * BG_KS;
+    const int rlim = (int)min((int64_t)(BG_KS - 1), r1 - 1 - rs);
+    bg_issue<QK>(g, dp, qt, rs, rlim, ring + (uint32_t)(slot_kt % BG_STAGES) * BG_SB, wave);
+  };
+
+#pragma unroll
+  for (int s = 0; s < BG_STAGES - 1; ++s) issue(s, s);
+
+  for (;;) {
+    f32x16_t acc[BG_BI][BG_BJ];
+#pragma unroll
+    for (int a = 0; a < BG_BI; ++a)
+#pragma unroll
+      for (int b = 0; b < BG_BJ; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    const int rem = (int)(r1 - r0 - (int64_t)(nk - 1) * BG_KS);  // rows of the last stage
+    const int nfull = rem == BG_KS ? nk : nk - 1;
+    for (int kt = 0; kt < nk; ++kt) {
+      vm_wait<(BG_STAGES - 2) * BG_LPS>();
+      barrier();
+      // slot (kt + STAGES - 1) % STAGES was read in iteration kt - 1, and every
+      // wave has passed the barrier since
+      issue(kt + BG_STAGES - 1, kt + BG_STAGES - 1);
+      const uint32_t cur = ring + (uint32_t)(kt % BG_STAGES) * BG_SB;
+      if (kt < nfull) bg_mma<QK, false>(acc, cur, fr, lane, BG_KS);
+      else bg_mma<QK, true>(acc, cur, fr, lane, rem);
+    }
+
+    const int un = u + gridDim.x;
+    const bool more = un < gr.total;
+    const int zc = z, i0c = i0, j0c = j0;
+    vm_wait<0>();
+    barrier();
+    if (more) {
+      bg_coords(gr, un, z, ti, tj);
+      i0 = ti * BG_TI;
+      j0 = tj * BG_TJ;
+      r0 = (int64_t)z * g.sps * BG_KS;
+      r1 = min(g.R, r0 + (int64_t)g.sps * BG_KS);
+      nk = (int)((r1 - r0 + BG_KS - 1) / BG_KS);
+      dp = bg_dma<QK>(g, i0, j0, wave, lane);
+      qt = g.q + (int64_t)j0 * g.ldq;
+#pragma unroll
+      for (int s = 0; s < BG_STAGES - 1; ++s) issue(s, s);
+    }
+    bg_store(g, acc, zc, i0c, j0c, wi, wj, lane);
+    if (!more) break;
+    u = un;
+  }
+}
+
+int bg_grid(const BGemm& g, int cus) {
+  const int64_t tiles = (int64_t)((g.I + BG_TI - 1) / BG_TI) * ((g.J + BG_TJ - 1) / BG_TJ) * g.splits;
+  int64_t n = (int64_t)(cus > 0 ? cus : 256) * BG_WG_PER_CU;
+  n -= n % 8;
+  if (n < 8) n = 8;
+  return (int)(tiles < n ? tiles : n);
 }
 
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int splits,
@@ -368,21 +528,36 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// Reduction splits of the dX GEMM: the split count s (1..8) whose rounds of
+// resident workgroups cover the work in the least time, ceil(tiles s / slots)
+// rounds of ceil(stages / s) stages, preferring fewer splits (each split adds
+// an fp32 partial of dX to write and reduce) and at least 8 stages per split.
+static int dx_split_count(int64_t T, int N, int K) {
+  const int64_t tiles = ((T + BG_TJ - 1) / BG_TJ) * ((K + BG_TI - 1) / BG_TI);
+  const int64_t stages = (N + BG_KS - 1) / BG_KS;
+  const int cus = device_cu_count();
+  const int64_t slots = (int64_t)(cus > 0 ? cus : 256) * BG_WG_PER_CU;
+  int best = 1;
+  int64_t best_cost = ((tiles + slots - 1) / slots) * stages;
+  for (int s = 2; s <= 8; ++s) {
+    const int64_t sps = (stages + s - 1) / s;
+    if (sps < 8) break;
+    const int64_t cost = ((tiles * s + slots - 1) / slots) * sps;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  const int64_t sps = (stages + best - 1) / best;
+  return (int)((stages + sps - 1) / sps);  // no empty split
+}
+
 BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx) {
   BwdPlan pl{};
   pl.db_row_chunks = (int)((T + IR_ROWS - 1) / IR_ROWS);
   pl.db_off = 0;
   pl.db_bytes = use_bias ? align256((size_t)pl.db_row_chunks * N * 4) : 0;
-  pl.dx_splits = 1;
-  if (want_dx && T > 0) {
-    const int64_t tiles = ((T + G_BM - 1) / G_BM) * ((K + G_BN - 1) / G_BN);
-    int64_t s = (640 + tiles - 1) / tiles;
-    const int64_t max_by_len = N / 1024;
-    if (s > max_by_len) s = max_by_len;
-    if (s > 8) s = 8;
-    if (s < 1) s = 1;
-    pl.dx_splits = (int)s;
-  }
+  pl.dx_splits = want_dx && T > 0 ? dx_split_count(T, N, K) : 1;
   pl.dx_off = pl.db_bytes;
   pl.dx_bytes = pl.dx_splits > 1 ? align256((size_t)pl.dx_splits * T * K * 4) : 0;
   pl.total = pl.db_bytes + pl.dx_bytes;
@@ -409,47 +584,50 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const int cus = device_cu_count();
   if (p.dx) {
-    GemmArgs g{};
-    g.a = p.dq_pre;
-    g.lda = p.N;
-    g.b = p.w;
-    g.ldb = p.K;
-    g.M = (int)p.T;
-    g.Nc = p.K;
+    // dX[t][k] = sum_n W[n][k] dq_pre[t][n]; the reduction length N is a
+    // multiple of 32, as a K-major Q requires
+    BGemm g{};
+    g.p = reinterpret_cast<const uint8_t*>(p.w);
+    g.ldp = (int64_t)p.K * 2;
+    g.q = reinterpret_cast<const uint8_t*>(p.dq_pre);
+    g.ldq = (int64_t)p.N * 2;
+    g.I = p.K;
+    g.J = (int)p.T;
     g.R = p.N;
-    const int64_t per = (((int64_t)p.N + pl.dx_splits - 1) / pl.dx_splits + 63) / 64 * 64;
-    g.r_per_split = per;
-    const bool split = pl.dx_splits > 1;
-    g.c = split ? static_cast<void*>(ws + pl.dx_off) : static_cast<void*>(p.dx);
+    const int stages = (p.N + BG_KS - 1) / BG_KS;
+    g.splits = pl.dx_splits;
+    g.sps = (stages + g.splits - 1) / g.splits;
+    const bool split = g.splits > 1;
+    g.out = split ? static_cast<void*>(ws + pl.dx_off) : static_cast<void*>(p.dx);
     g.out_f32 = split ? 1 : 0;
-    const int tiles = ((g.M + G_BM - 1) / G_BM) * ((g.Nc + G_BN - 1) / G_BN);
-    hipLaunchKernelGGL((gemm_kernel<true, false>), dim3(tiles, 1, pl.dx_splits), dim3(G_THREADS), 0,
-                       stream, g);
+    hipLaunchKernelGGL(bgemm_kernel<true>, dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (split) {
       const int64_t n4 = p.T * p.K / 4;
       hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                         static_cast<const float*>(g.c), pl.dx_splits, n4, p.dx);
+                         static_cast<const float*>(g.out), g.splits, n4, p.dx);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
   if (p.dw) {
-    GemmArgs g{};
-    g.a = p.dq_pre;
-    g.lda = p.N;
-    g.b = p.x;
-    g.ldb = p.K;
-    g.M = p.N;
-    g.Nc = p.K;
+    // dW[n][k] = sum_t X[t][k] dq_pre[t][n]
+    BGemm g{};
+    g.p = reinterpret_cast<const uint8_t*>(p.x);
+    g.ldp = (int64_t)p.K * 2;
+    g.q = reinterpret_cast<const uint8_t*>(p.dq_pre);
+    g.ldq = (int64_t)p.N * 2;
+    g.I = p.K;
+    g.J = p.N;
     g.R = p.T;
-    g.r_per_split = p.T;
-    g.c = p.dw;
+    g.splits = 1;
+    g.sps = (int)((p.T + BG_KS - 1) / BG_KS);
+    g.out = p.dw;
     g.out_f32 = p.dw_fp32;
-    const int tiles = ((g.M + G_BM - 1) / G_BM) * ((g.Nc + G_BN - 1) / G_BN);
-    hipLaunchKernelGGL((gemm_kernel<false, false>), dim3(tiles, 1, 1), dim3(G_THREADS), 0, stream, g);
+    hipLaunchKernelGGL(bgemm_kernel<false>, dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

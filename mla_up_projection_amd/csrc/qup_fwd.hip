@@ -65,30 +65,6 @@ __device__ __forceinline__ int roff(int r, int c) { return r * ROWB + ((c ^ swz(
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Direct global->LDS copy of 16 bytes per lane: lane i of the wave writes
-// LDS bytes [lds_addr + 16 i, +16) from global sbase + voff.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(sbase)
-               : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
-}
-
 // ---------------------------------------------------------------------------
 // Fused epilogue for one 32 (n) x 32 (token) accumulator block.
 // acc[r] holds row 8*(r/4) + 4*(lane/32) + r%4 of the block, token lane%32.
