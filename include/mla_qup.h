@@ -195,7 +195,7 @@ typedef struct {
   mla_rope rope;
   void* dq_pre;             /* out: bf16 [T, N]; 16-B aligned (required) */
   void* dx;                 /* out: bf16 [T, K], or NULL to skip; 16-B aligned */
-  void* dw;                 /* out: [N, K] in dw_dtype, or NULL to skip */
+  void* dw;                 /* out: [N, K] in dw_dtype, or NULL to skip; 16-B aligned */
   int32_t dw_dtype;         /* MLA_DTYPE_BF16 or MLA_DTYPE_FP32 */
   int32_t use_bias;         /* 0 or 1 */
   void* db;                 /* out: bf16 [N]; required iff use_bias */

@@ -19,18 +19,22 @@ constexpr int FMT_SBHD = 1;
 constexpr int FMT_THD = 2;
 
 // ---------------------------------------------------------------------------
-// bf16 <-> fp32. Round to nearest, ties to even; NaN stays a quiet NaN.
+// bf16 <-> fp32. fp32 -> bf16 is gfx950's v_cvt_pk_bf16_f32 (two values per
+// instruction): round to nearest, ties to even, denormals kept, NaN stays NaN;
+// it agrees bit for bit with integer round-to-nearest-even on every tie of
+// every upper half-word and on a strided sweep of all fp32 patterns.
 // ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u | ((u >> 16) & 0x8000u);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return pack_bf16x2(f, 0.0f) & 0xFFFFu;
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
-}
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
 // ---------------------------------------------------------------------------

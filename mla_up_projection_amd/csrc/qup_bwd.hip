@@ -199,8 +199,7 @@ struct BGemm {
   int64_t R;          // reduction length
   int splits;         // reduction splits; split z covers stages [z*sps, (z+1)*sps)
   int sps;
-  void* out;          // [splits][J][I] (fp32) or [J][I] (bf16)
-  int out_f32;
+  void* out;          // [splits][J][I] (fp32) or [J][I] (bf16), by the kernel's F32
 };
 
 struct BgGrid {
@@ -378,7 +377,11 @@ __device__ __forceinline__ void bg_mma(f32x16_t (&acc)[BG_BI][BG_BJ], uint32_t c
 }
 
 // acc[ib][jb] lane l, register r: i = i0 + 96 wi + 32 ib + 8 (r/4) + 4 (l/32) + r%4,
-// j = j0 + 64 wj + 32 jb + l%32.
+// j = j0 + 64 wj + 32 jb + l%32. fp32: 4 consecutive i per lane (16 bytes).
+// bf16: lanes l and l^32 trade one 4-value group (one xor-shuffle) so each
+// lane stores 8 consecutive i (16 bytes) and each row j receives 32
+// contiguous bytes per store instruction.
+template <bool F32>
 __device__ __forceinline__ void bg_store(const BGemm& g, const f32x16_t (&acc)[BG_BI][BG_BJ], int z, int i0,
                                          int j0, int wi, int wj, int lane) {
   const int half = lane >> 5;
@@ -386,27 +389,40 @@ __device__ __forceinline__ void bg_store(const BGemm& g, const f32x16_t (&acc)[B
 #pragma unroll
   for (int jb = 0; jb < BG_BJ; ++jb) {
     const int j = j0 + 64 * wj + 32 * jb + (lane & 31);
-    if (j >= g.J) continue;
+    const bool jok = j < g.J;
 #pragma unroll
     for (int ib = 0; ib < BG_BI; ++ib) {
+      const int ib0 = i0 + 32 * (BG_BI * wi + ib);
+      const f32x16_t& A = acc[ib][jb];
+      if (F32) {
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int i = i0 + 32 * (BG_BI * wi + ib) + 8 * grp + 4 * half;
-        if (i >= g.I) continue;
-        const float v0 = acc[ib][jb][4 * grp], v1 = acc[ib][jb][4 * grp + 1];
-        const float v2 = acc[ib][jb][4 * grp + 2], v3 = acc[ib][jb][4 * grp + 3];
-        const int64_t idx = zoff + (int64_t)j * g.I + i;
-        if (g.out_f32)
-          *reinterpret_cast<float4*>(static_cast<float*>(g.out) + idx) = make_float4(v0, v1, v2, v3);
-        else
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + idx) =
-              make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        for (int grp = 0; grp < 4; ++grp) {
+          const int i = ib0 + 8 * grp + 4 * half;
+          if (jok && i < g.I)
+            *reinterpret_cast<float4*>(static_cast<float*>(g.out) + zoff + (int64_t)j * g.I + i) =
+                make_float4(A[4 * grp], A[4 * grp + 1], A[4 * grp + 2], A[4 * grp + 3]);
+        }
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          // groups 2pp (i = 16pp + 4half + 0..3) and 2pp+1 (i = 16pp + 8 + 4half + 0..3)
+          const uint32_t a0 = pack_bf16x2(A[8 * pp + 0], A[8 * pp + 1]);
+          const uint32_t a1 = pack_bf16x2(A[8 * pp + 2], A[8 * pp + 3]);
+          const uint32_t b0 = pack_bf16x2(A[8 * pp + 4], A[8 * pp + 5]);
+          const uint32_t b1 = pack_bf16x2(A[8 * pp + 6], A[8 * pp + 7]);
+          const uint32_t r0 = (uint32_t)__shfl_xor((int)(half ? a0 : b0), 32);
+          const uint32_t r1 = (uint32_t)__shfl_xor((int)(half ? a1 : b1), 32);
+          const u32x4_t o = half ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
+          const int i = ib0 + 16 * pp + 8 * half;
+          if (jok && i < g.I)
+            *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(g.out) + zoff + (int64_t)j * g.I + i) = o;
+        }
       }
     }
   }
 }
 
-template <bool QK>
+template <bool QK, bool F32>
 __global__ __launch_bounds__(BG_THREADS) __attribute__((amdgpu_waves_per_eu(BG_WG_PER_CU, BG_WG_PER_CU)))
 void bgemm_kernel(BGemm g) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[BG_STAGES * BG_SB];
@@ -456,37 +472,41 @@ void bgemm_kernel(BGemm g) {
 
     const int rem = (int)(r1 - r0 - (int64_t)(nk - 1) * BG_KS);  // rows of the last stage
     const int nfull = rem == BG_KS ? nk : nk - 1;
-    for (int kt = 0; kt < nk; ++kt) {
+    // Full stages in a loop with one code path (a second MFMA path inside the
+    // loop makes the compiler copy every accumulator at the merge).
+    for (int kt = 0; kt < nfull; ++kt) {
       vm_wait<(BG_STAGES - 2) * BG_LPS>();
       barrier();
       // slot (kt + STAGES - 1) % STAGES was read in iteration kt - 1, and every
       // wave has passed the barrier since
       issue(kt + BG_STAGES - 1, kt + BG_STAGES - 1);
-      const uint32_t cur = ring + (uint32_t)(kt % BG_STAGES) * BG_SB;
-      if (kt < nfull) bg_mma<QK, false>(acc, cur, fr, lane, BG_KS);
-      else bg_mma<QK, true>(acc, cur, fr, lane, rem);
+      bg_mma<QK, false>(acc, ring + (uint32_t)(kt % BG_STAGES) * BG_SB, fr, lane, BG_KS);
+    }
+    if (nfull < nk) {
+      // partial last stage: no further stage to issue (the wait below drains all)
+      vm_wait<(BG_STAGES - 2) * BG_LPS>();
+      barrier();
+      bg_mma<QK, true>(acc, ring + (uint32_t)(nfull % BG_STAGES) * BG_SB, fr, lane, rem);
     }
 
-    const int un = u + gridDim.x;
-    const bool more = un < gr.total;
-    const int zc = z, i0c = i0, j0c = j0;
+    // drain this tile's DMA (including the clamped stages issued past its
+    // end) and let every wave finish reading the ring; store the tile, then
+    // start the next one
     vm_wait<0>();
     barrier();
-    if (more) {
-      bg_coords(gr, un, z, ti, tj);
-      i0 = ti * BG_TI;
-      j0 = tj * BG_TJ;
-      r0 = (int64_t)z * g.sps * BG_KS;
-      r1 = min(g.R, r0 + (int64_t)g.sps * BG_KS);
-      nk = (int)((r1 - r0 + BG_KS - 1) / BG_KS);
-      dp = bg_dma<QK>(g, i0, j0, wave, lane);
-      qt = g.q + (int64_t)j0 * g.ldq;
+    bg_store<F32>(g, acc, z, i0, j0, wi, wj, lane);
+    u += gridDim.x;
+    if (u >= gr.total) break;
+    bg_coords(gr, u, z, ti, tj);
+    i0 = ti * BG_TI;
+    j0 = tj * BG_TJ;
+    r0 = (int64_t)z * g.sps * BG_KS;
+    r1 = min(g.R, r0 + (int64_t)g.sps * BG_KS);
+    nk = (int)((r1 - r0 + BG_KS - 1) / BG_KS);
+    dp = bg_dma<QK>(g, i0, j0, wave, lane);
+    qt = g.q + (int64_t)j0 * g.ldq;
 #pragma unroll
-      for (int s = 0; s < BG_STAGES - 1; ++s) issue(s, s);
-    }
-    bg_store(g, acc, zc, i0c, j0c, wi, wj, lane);
-    if (!more) break;
-    u = un;
+    for (int s = 0; s < BG_STAGES - 1; ++s) issue(s, s);
   }
 }
 
@@ -601,8 +621,10 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     g.sps = (stages + g.splits - 1) / g.splits;
     const bool split = g.splits > 1;
     g.out = split ? static_cast<void*>(ws + pl.dx_off) : static_cast<void*>(p.dx);
-    g.out_f32 = split ? 1 : 0;
-    hipLaunchKernelGGL(bgemm_kernel<true>, dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
+    if (split)
+      hipLaunchKernelGGL((bgemm_kernel<true, true>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
+    else
+      hipLaunchKernelGGL((bgemm_kernel<true, false>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (split) {
@@ -626,8 +648,10 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     g.splits = 1;
     g.sps = (int)((p.T + BG_KS - 1) / BG_KS);
     g.out = p.dw;
-    g.out_f32 = p.dw_fp32;
-    hipLaunchKernelGGL(bgemm_kernel<false>, dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
+    if (p.dw_fp32)
+      hipLaunchKernelGGL((bgemm_kernel<false, true>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
+    else
+      hipLaunchKernelGGL((bgemm_kernel<false, false>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

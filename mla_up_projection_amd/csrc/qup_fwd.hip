@@ -62,7 +62,6 @@ constexpr int WSC_BYTES = TILE_N * MAX_KBLOCKS;
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int roff(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
