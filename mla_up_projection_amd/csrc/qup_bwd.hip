@@ -355,6 +355,10 @@ __device__ __forceinline__ void bg_mma(f32x16_t (&acc)[BG_BI][BG_BJ], uint32_t c
       }
     }
   }
+  // keep every fragment read of the stage ahead of its MFMAs: the second
+  // k16 step's reads then complete under the first step's MFMAs (the default
+  // schedule interleaves each read right before its use)
+  __builtin_amdgcn_sched_barrier(0);
   if (TAIL) {
 #pragma unroll
     for (int js = 0; js < 2; ++js) {

@@ -352,6 +352,7 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
       for (int tb = 0; tb < WBLK_T; ++tb)
         b[j][tb] = *reinterpret_cast<const bf16x8_t*>(cur + roff(brow0 + 32 * tb, 2 * j + half));
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead (see comment above)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
