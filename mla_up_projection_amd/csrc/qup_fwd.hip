@@ -12,12 +12,13 @@
 // Work decomposition (two independent 256-thread workgroups per CU, persistent,
 // so each SIMD runs one wave of each: one workgroup's barriers, LDS round trips
 // and epilogue are covered by the other's MFMAs):
-//   * tile = 128 tokens x 192 rows of N (one DeepSeek-V3 head); each of the 4
-//     waves owns 32 tokens x all 192 rows = 6 blocks of the 32x32 MFMA, 96
-//     fp32 accumulators per lane, so a lane pair holds a token's whole head. The MFMA row axis is N (W is the A operand), so
-//     a lane holds runs of 4 consecutive head-dim elements of one token:
-//     RoPE pairs are lane-local and a 32-element scale block is split
-//     between lanes l and l^32 (one xor-shuffle for its amax).
+//   * tile = 128 tokens x 192 rows of N (one DeepSeek-V3 head); the 4 waves
+//     form 2 x 2, each owning 64 tokens x 96 rows = 2 x 3 blocks of the
+//     32x32 MFMA (96 fp32 accumulators per lane; 5 fragment reads per 6
+//     MFMAs). The MFMA row axis is N (W is the A operand), so a lane holds
+//     runs of 4 consecutive head-dim elements of one token: RoPE pairs are
+//     lane-local and a 32-element scale block is split between lanes l and
+//     l^32 (one xor-shuffle for its amax).
 //   * K streams through an LDS ring (4 slots for bf16, 3 for E4M3) of 64-byte
 //     row slices (32 bf16 or 64 E4M3 K-values per row per stage), filled by
 //     direct global->LDS DMA (global_load_lds_dwordx4) issued STAGES-1
@@ -49,8 +50,11 @@ constexpr int STAGES_MX = 3;              // 60 KB + 20 KB of operand scales
 constexpr int LQX = XSB / 1024 / 4;       // X DMA loads per wave per stage (1 KB each)
 constexpr int LQW = WSB / 1024 / 4;       // W DMA loads per wave per stage
 constexpr int LPS = LQX + LQW;            // DMA loads per wave per stage
-constexpr int WBLK_N = TILE_N / 32;       // 32-row blocks per wave (all rows of the tile)
-constexpr int WBLK_T = 1;                 // 32-token blocks per wave (32 tokens)
+constexpr int WBLK_N = 3;                 // 32-row blocks of N per wave (96 rows)
+constexpr int WBLK_T = 2;                 // 32-token blocks per wave (64 tokens)
+constexpr int WAVES_N = TILE_N / (32 * WBLK_N);  // waves along N (2); along T: 2
+static_assert(WAVES_N * (TILE_T / (32 * WBLK_T)) == NTHREADS / 64, "2 x 2 waves");
+static_assert(WBLK_N == 3, "packed scale stores below are written for 3 blocks per wave");
 constexpr int WG_PER_CU = 2;              // two independent workgroups per CU
 constexpr int MAX_KBLOCKS = 64;           // MXFP8: K <= 2048 (operand scales of a tile live in LDS)
 constexpr int XSC_BYTES = TILE_T * MAX_KBLOCKS;
@@ -218,10 +222,16 @@ __device__ __forceinline__ void epilogue_tok(const FwdParams& p, const TokenMap&
   uint32_t sc[WBLK_N];
   (epilogue_one<TB, NBs>(p, ti, acc, n0, lane, packed, sc), ...);
   if (packed && ti.ok && lane < 32) {
+    // this wave's 3 scale bytes of the token's head: one 16-bit and one byte store
     const int64_t row = ti.row + (int64_t)(n0 / p.D) * p.S;
-    uint16_t* dst = reinterpret_cast<uint16_t*>(p.out_scales + row * (TILE_N / 32));
-#pragma unroll
-    for (int k = 0; k < WBLK_N / 2; ++k) dst[k] = (uint16_t)(sc[2 * k] | (sc[2 * k + 1] << 8));
+    uint8_t* dst = p.out_scales + row * (TILE_N / 32) + (n0 % p.D) / 32;
+    if ((reinterpret_cast<uintptr_t>(dst) & 1) == 0) {
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(sc[0] | (sc[1] << 8));
+      dst[2] = (uint8_t)sc[2];
+    } else {
+      dst[0] = (uint8_t)sc[0];
+      *reinterpret_cast<uint16_t*>(dst + 1) = (uint16_t)(sc[1] | (sc[2] << 8));
+    }
   }
 }
 
@@ -463,8 +473,9 @@ void qup_fwd_kernel(FwdParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
-  const int arow0 = lane & 31;               // every wave covers all TILE_N rows
-  const int brow0 = 32 * wave + (lane & 31);  // and 32 of the tile's tokens
+  const int wn = wave % WAVES_N, wt = wave / WAVES_N;
+  const int arow0 = 32 * WBLK_N * wn + (lane & 31);  // 96 of the tile's N rows
+  const int brow0 = 32 * WBLK_T * wt + (lane & 31);  // and 64 of its tokens
 
   const TileGrid grid{(int)((p.T + TILE_T - 1) / TILE_T), (p.N + TILE_N - 1) / TILE_N, 0};
   const TileGrid g{grid.tiles_t, grid.tiles_n, grid.tiles_t * grid.tiles_n};
@@ -526,7 +537,7 @@ void qup_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int s = 0; s < STAGES - 1; ++s) issue_stage<STAGES>(dp, xb, wb, s, nk, s, ring, wave);
     }
-    epilogue_tile(p, tm, acc, n0c, t0c + 32 * wave + (lane & 31), lane);
+    epilogue_tile(p, tm, acc, n0c + 32 * WBLK_N * wn, t0c + 32 * WBLK_T * wt + (lane & 31), lane);
     if (!more) break;
     u = un;
     if (MX) {
