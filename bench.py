@@ -31,7 +31,9 @@ BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 METRIC = "fused Q-up-proj fwd/bwd TFLOP/s and % MFMA peak at DeepSeek-V3 shape, 1 GPU"
-FWD_KERNEL_SRC = os.path.join(ROOT, "mla_up_projection_amd", "csrc", "qup_fwd.hip")
+# sources compiled into the fused forward kernel (its traffic summary is tied to them)
+FWD_KERNEL_SRCS = [os.path.join(ROOT, "mla_up_projection_amd", "csrc", f)
+                   for f in ("qup_fwd.hip", "device_common.h", "internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qup_fwd_bf16_dsv3_traffic.md")
 
 
@@ -48,7 +50,14 @@ def parse_args():
     return ap.parse_args()
 
 
-def fwd_traffic(n_launch_bytes_alg: float):
+def fwd_kernel_sha256() -> str:
+    h = hashlib.sha256()
+    for f in FWD_KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def fwd_traffic():
     """HBM bytes per launch of the fused forward from the committed counter
     summary, or None if it is absent or was taken on another kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -58,8 +67,7 @@ def fwd_traffic(n_launch_bytes_alg: float):
     m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
     if not m_bytes or not m_src:
         return None
-    cur = hashlib.sha256(open(FWD_KERNEL_SRC, "rb").read()).hexdigest()
-    if cur != m_src.group(1):
+    if fwd_kernel_sha256() != m_src.group(1):
         return None
     return float(m_bytes.group(1))
 
@@ -186,7 +194,7 @@ def main():
         torch.cuda.synchronize()
         parts["calib_copy_bytes"] = n
 
-    traffic = fwd_traffic(flops_fwd)
+    traffic = fwd_traffic()
     roofline = {"bound": "mfma", "kernel": "qup_fwd_kernel<bf16> (fused GEMM+RoPE+MXFP8)",
                 "achieved": fwd_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": fwd_tflops / BF16_PEAK_TFLOPS, "traffic": traffic}

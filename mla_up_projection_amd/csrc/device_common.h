@@ -38,6 +38,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
 }
 
 // ---------------------------------------------------------------------------
+// Exchange between the two halves of a wave (gfx950 v_permlane32_swap): the
+// upper 32 lanes of `a` trade places with the lower 32 lanes of `b`. Lane l
+// < 32 gets {a[l], a[l + 32]}; lane l >= 32 gets {b[l - 32], b[l]}.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2_t swap_halves(uint32_t a, uint32_t b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return u32x2_t{r[0], r[1]};
+}
+
+// ---------------------------------------------------------------------------
 // MXFP8 (OCP Microscaling Formats v1.0, E4M3 elements, E8M0 scales).
 // The block exponent comes from the float32 bit pattern of amax by integer
 // arithmetic, so it does not depend on the denormal mode of the FP unit.

@@ -382,7 +382,7 @@ __device__ __forceinline__ void bg_mma(f32x16_t (&acc)[BG_BI][BG_BJ], uint32_t c
 
 // acc[ib][jb] lane l, register r: i = i0 + 96 wi + 32 ib + 8 (r/4) + 4 (l/32) + r%4,
 // j = j0 + 64 wj + 32 jb + l%32. fp32: 4 consecutive i per lane (16 bytes).
-// bf16: lanes l and l^32 trade one 4-value group (one xor-shuffle) so each
+// bf16: lanes l and l^32 trade one 4-value group (v_permlane32_swap) so each
 // lane stores 8 consecutive i (16 bytes) and each row j receives 32
 // contiguous bytes per store instruction.
 template <bool F32>
@@ -414,9 +414,9 @@ __device__ __forceinline__ void bg_store(const BGemm& g, const f32x16_t (&acc)[B
           const uint32_t a1 = pack_bf16x2(A[8 * pp + 2], A[8 * pp + 3]);
           const uint32_t b0 = pack_bf16x2(A[8 * pp + 4], A[8 * pp + 5]);
           const uint32_t b1 = pack_bf16x2(A[8 * pp + 6], A[8 * pp + 7]);
-          const uint32_t r0 = (uint32_t)__shfl_xor((int)(half ? a0 : b0), 32);
-          const uint32_t r1 = (uint32_t)__shfl_xor((int)(half ? a1 : b1), 32);
-          const u32x4_t o = half ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
+          // lower lane: own a, partner's a; upper lane: partner's b, own b
+          const u32x2_t s0 = swap_halves(a0, b0), s1 = swap_halves(a1, b1);
+          const u32x4_t o = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
           const int i = ib0 + 16 * pp + 8 * half;
           if (jok && i < g.I)
             *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(g.out) + zoff + (int64_t)j * g.I + i) = o;

@@ -66,7 +66,6 @@ constexpr int WSC_BYTES = TILE_N * MAX_KBLOCKS;
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int roff(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
 
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Fused epilogue for one 32 (n) x 32 (token) accumulator block.
@@ -102,38 +101,57 @@ __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const Tok
   for (int r = 0; r < 16; ++r) v[r] = acc[r];
 
   if (p.bias) {
+    // rows 8g + 4 half + 0..3 of this lane: 4 consecutive bf16 (8 bytes, N % 32 == 0)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int n = n_blk + 8 * (r >> 2) + 4 * half + (r & 3);
-      v[r] += bf16_bits_to_f32(p.bias[n]);
+    for (int g = 0; g < 4; ++g) {
+      const uint2 bb = *reinterpret_cast<const uint2*>(p.bias + n_blk + 8 * g + 4 * half);
+      v[4 * g] += bf16_bits_to_f32(bb.x & 0xFFFFu);
+      v[4 * g + 1] += bf16_bits_to_f32(bb.x >> 16);
+      v[4 * g + 2] += bf16_bits_to_f32(bb.y & 0xFFFFu);
+      v[4 * g + 3] += bf16_bits_to_f32(bb.y >> 16);
     }
   }
   if (d_blk + 32 > p.d_nope && p.d_rope > 0) {
     const bool pos_ok = ti.ok && ti.pos >= 0 && ti.pos < p.rope_rows;
     const int64_t trow = (int64_t)(pos_ok ? ti.pos : 0) * p.rope_pairs;
-    // rows 4g + {0,1} and 4g + {2,3} of this lane are pairs i, i+1 of the
-    // table: one 8-byte load each when they are 8-byte aligned
-    const bool vec = ((p.d_nope | p.rope_pairs) & 1) == 0 && (p.d_nope & 3) == 0;
+    const float nan = __builtin_nanf("");
+    // Rows 4g + {0,1} and 4g + {2,3} of this lane are table pairs i, i+1.
+    if (d_blk >= p.d_nope && ((p.d_nope | p.rope_pairs) & 3) == 0) {
+      // Whole block inside the rope slice (uniform branch): pair index
+      // i = i0 + 4g with i0 even, so each group is one 8-byte cos and one
+      // 8-byte sin load, all eight issued before any use.
+      const int i0 = ((d_blk - p.d_nope) >> 1) + 2 * half;
+      float2 cc[4], ss[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = d_blk + 8 * g + 4 * half;
-      if (d >= p.d_nope) {
-        const int i = (d - p.d_nope) >> 1;
-        float c0, c1, s0, s1;
-        if (vec) {
-          const float2 cc = *reinterpret_cast<const float2*>(p.cos + trow + i);
-          const float2 ss = *reinterpret_cast<const float2*>(p.sin + trow + i);
-          c0 = cc.x; c1 = cc.y; s0 = ss.x; s1 = ss.y;
-        } else {
-          c0 = p.cos[trow + i]; c1 = p.cos[trow + i + 1];
-          s0 = p.sin[trow + i]; s1 = p.sin[trow + i + 1];
-        }
-        if (!pos_ok) c0 = c1 = s0 = s1 = __builtin_nanf("");
+      for (int g = 0; g < 4; ++g) {
+        cc[g] = *reinterpret_cast<const float2*>(p.cos + trow + i0 + 4 * g);
+        ss[g] = *reinterpret_cast<const float2*>(p.sin + trow + i0 + 4 * g);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float c0 = pos_ok ? cc[g].x : nan, c1 = pos_ok ? cc[g].y : nan;
+        const float s0 = pos_ok ? ss[g].x : nan, s1 = pos_ok ? ss[g].y : nan;
         const float a0 = v[4 * g], b0 = v[4 * g + 1], a1 = v[4 * g + 2], b1 = v[4 * g + 3];
         v[4 * g] = a0 * c0 - b0 * s0;
         v[4 * g + 1] = a0 * s0 + b0 * c0;
         v[4 * g + 2] = a1 * c1 - b1 * s1;
         v[4 * g + 3] = a1 * s1 + b1 * c1;
+      }
+    } else {
+      // block straddling the nope/rope boundary, or unaligned table rows
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = d_blk + 8 * g + 4 * half;
+        if (d >= p.d_nope) {
+          const int i = (d - p.d_nope) >> 1;
+          const float c0 = pos_ok ? p.cos[trow + i] : nan, c1 = pos_ok ? p.cos[trow + i + 1] : nan;
+          const float s0 = pos_ok ? p.sin[trow + i] : nan, s1 = pos_ok ? p.sin[trow + i + 1] : nan;
+          const float a0 = v[4 * g], b0 = v[4 * g + 1], a1 = v[4 * g + 2], b1 = v[4 * g + 3];
+          v[4 * g] = a0 * c0 - b0 * s0;
+          v[4 * g + 1] = a0 * s0 + b0 * c0;
+          v[4 * g + 2] = a1 * c1 - b1 * s1;
+          v[4 * g + 3] = a1 * s1 + b1 * c1;
+        }
       }
     }
   }
@@ -144,7 +162,8 @@ __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const Tok
     uint32_t m = 0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) m = max(m, abs_bits(v[r]));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+    const u32x2_t mm = swap_halves(m, m);
+    m = max(mm[0], mm[1]);  // amax over both halves of the block
     uint32_t P[4];
     if (m >= 0x7F800000u) {
       P[0] = P[1] = P[2] = P[3] = 0x7F7F7F7Fu;
@@ -155,16 +174,13 @@ __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const Tok
       for (int g = 0; g < 4; ++g) P[g] = e4m3_pack4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], E);
       sc = (uint32_t)(E + 127);
     }
-    // Lanes l and l+32 swap two 4-row groups so each ends up with 16
+    // Lanes l and l+32 trade two 4-row groups so each ends up with 16
     // consecutive rows: lower lane rows 0..15, upper lane rows 16..31.
-    const uint32_t s0 = half ? P[0] : P[2];
-    const uint32_t s1 = half ? P[1] : P[3];
-    const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32);
-    const uint32_t r1 = (uint32_t)__shfl_xor((int)s1, 32);
-    u32x4_t o = half ? u32x4_t{r0, P[2], r1, P[3]} : u32x4_t{P[0], r0, P[1], r1};
+    const u32x2_t o01 = swap_halves(P[0], P[2]);
+    const u32x2_t o23 = swap_halves(P[1], P[3]);
     if (ti.ok) {
       uint8_t* dst = static_cast<uint8_t*>(p.out) + row * p.D + d_blk + 16 * half;
-      *reinterpret_cast<u32x4_t*>(dst) = o;
+      *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{o01[0], o01[1], o23[0], o23[1]};
       if (store_scale && half == 0) p.out_scales[row * (p.D / 32) + d_blk / 32] = (uint8_t)sc;
     }
   } else {
@@ -174,23 +190,14 @@ __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const Tok
       P[2 * g] = pack_bf16x2(v[4 * g + 0], v[4 * g + 1]);
       P[2 * g + 1] = pack_bf16x2(v[4 * g + 2], v[4 * g + 3]);
     }
-    uint32_t snd[4], rcv[4];
+    // lower lane: rows 0..7 then 8..15; upper lane: rows 16..23 then 24..31
+    u32x2_t r[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) snd[k] = half ? P[k] : P[4 + k];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) rcv[k] = (uint32_t)__shfl_xor((int)snd[k], 32);
-    u32x4_t o0, o1;
-    if (half) {
-      o0 = u32x4_t{rcv[0], rcv[1], P[4], P[5]};
-      o1 = u32x4_t{rcv[2], rcv[3], P[6], P[7]};
-    } else {
-      o0 = u32x4_t{P[0], P[1], rcv[0], rcv[1]};
-      o1 = u32x4_t{P[2], P[3], rcv[2], rcv[3]};
-    }
+    for (int k = 0; k < 4; ++k) r[k] = swap_halves(P[k], P[4 + k]);
     if (ti.ok) {
       uint16_t* dst = static_cast<uint16_t*>(p.out) + row * p.D + d_blk + 16 * half;
-      reinterpret_cast<u32x4_t*>(dst)[0] = o0;
-      reinterpret_cast<u32x4_t*>(dst)[1] = o1;
+      reinterpret_cast<u32x4_t*>(dst)[0] = u32x4_t{r[0][0], r[1][0], r[0][1], r[1][1]};
+      reinterpret_cast<u32x4_t*>(dst)[1] = u32x4_t{r[2][0], r[3][0], r[2][1], r[3][1]};
     }
   }
   return sc;
