@@ -59,9 +59,13 @@ __global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, float
     pi[k] = rot[k] ? (d - p.d_nope) >> 1 : 0;
   }
   const bool any_rot = rot[0] || rot[1] || rot[2] || rot[3];
+  // all four pairs rotated and their table entries 16-byte aligned: one
+  // float4 of cos and one of sin per row
+  const bool vec4 = rot[0] && rot[3] && (pi[0] & 3) == 0 && (p.rope_pairs & 3) == 0;
   float sum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   // Rows in batches of RB: all loads of a batch are issued before any store,
-  // so RB 16-byte loads per lane are in flight at once.
+  // so RB 16-byte loads per lane are in flight at once. dq is read exactly
+  // once (non-temporal load); dq_pre is read again by the GEMMs.
   constexpr int RB = 8;
   for (int i0 = 0; i0 < rows; i0 += RB) {
     u32x4_t g[RB];
@@ -69,16 +73,26 @@ __global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, float
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const int i = i0 + j < rows ? i0 + j : rows - 1;
-      g[j] = *reinterpret_cast<const u32x4_t*>(dq + (r0 + i) * p.N + n0);
+      g[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(dq + (r0 + i) * p.N + n0));
       if (any_rot) {
         const int pos = s_pos[i];
         const bool pos_ok = pos >= 0 && pos < p.rope_rows;
         const int64_t trow = (int64_t)(pos_ok ? pos : 0) * p.rope_pairs;
+        if (vec4) {
+          const float4 c4 = *reinterpret_cast<const float4*>(cos_t + trow + pi[0]);
+          const float4 s4 = *reinterpret_cast<const float4*>(sin_t + trow + pi[0]);
+          cs[j][0] = c4.x; cs[j][1] = c4.y; cs[j][2] = c4.z; cs[j][3] = c4.w;
+          sn[j][0] = s4.x; sn[j][1] = s4.y; sn[j][2] = s4.z; sn[j][3] = s4.w;
+        } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          cs[j][k] = rot[k] ? cos_t[trow + pi[k]] : 1.0f;
-          sn[j][k] = rot[k] ? sin_t[trow + pi[k]] : 0.0f;
-          if (!pos_ok) cs[j][k] = sn[j][k] = __builtin_nanf("");
+          for (int k = 0; k < 4; ++k) {
+            cs[j][k] = rot[k] ? cos_t[trow + pi[k]] : 1.0f;
+            sn[j][k] = rot[k] ? sin_t[trow + pi[k]] : 0.0f;
+          }
+        }
+        if (!pos_ok) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) cs[j][k] = sn[j][k] = __builtin_nanf("");
         }
       }
     }
