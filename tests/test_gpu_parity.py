@@ -348,6 +348,33 @@ def test_bwd_thd_yarn_no_bias():
     assert frob_rel(o.to_f64(g["dw"].cpu()), r.dw) <= 1e-2
 
 
+def test_bwd_dx_only_and_dw_only():
+    """Only dX, then only dW: the separate-launch paths (both together share
+    one launch)."""
+    T, K, H = 301, 320, 3
+    x = syn.normal_bf16((T, K), 1.0, 80)
+    w = syn.normal_bf16((H * 192, K), 0.02, 81)
+    dq = syn.normal_bf16((T, H, 192), 1e-3, 82)
+    N = H * 192
+    cos, sin, oc, os_ = rope_tables(T, 64)
+    r = o.qup_backward(dq, x, w, H=H, d_nope=128, d_rope=64, cos=oc, sin=os_, S=T)
+    dqd, xd, wd = _dev(dq), _dev(x), _dev(w)
+    for want in ("dx", "dw"):
+        dq_pre = torch.empty(T, N, dtype=torch.bfloat16, device=DEV)
+        dx = torch.empty(T, K, dtype=torch.bfloat16, device=DEV) if want == "dx" else None
+        dw = torch.empty(N, K, dtype=torch.float32, device=DEV) if want == "dw" else None
+        kw = dict(H=H, d_nope=128, d_rope=64, cos=cos, sin=sin, dx=dx, dw=dw, db=None,
+                  use_bias=False, B=1, S=T)
+        nbytes = m.mla_qup_bwd_workspace_size(dqd, xd, wd, dq_pre, **kw)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+        m.mla_qup_bwd(dqd, xd, wd, dq_pre, workspace=ws if nbytes else None, **kw)
+        torch.cuda.synchronize()
+        if want == "dx":
+            assert frob_rel(o.to_f64(dx.cpu()), r.dx) <= 1e-2
+        else:
+            assert frob_rel(o.to_f64(dw.cpu()), r.dw) <= 1e-2
+
+
 def test_bwd_zero_tokens_zeroes_dw_db():
     K, H = 64, 2
     x = torch.empty(0, K, dtype=torch.bfloat16, device=DEV)
