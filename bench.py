@@ -40,8 +40,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qup_fwd_bf16_dsv3_traffic.md")
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--legs-reps", type=int, default=20)
@@ -125,12 +125,13 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         m.mla_qup_bwd(dq, x, w, dq_pre, workspace=ws, **bkw)
+        if ev is not None:
+            ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -138,7 +139,13 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    fwd_each = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    bwd_each = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    fwd_ms = float(np.mean(fwd_each))
+
+    def pct(a):
+        return {"median_ms": float(np.median(a)), "p10_ms": float(np.percentile(a, 10)),
+                "p90_ms": float(np.percentile(a, 90))}
 
     flops_fwd = 2.0 * T * N * K
     flops_bwd = 4.0 * T * N * K
@@ -159,8 +166,9 @@ def main():
         return a.elapsed_time(b) / reps
 
     parts = {"qup_fwd_bf16_dsv3": {"ms": fwd_ms, "tflops": fwd_tflops,
-                                   "pct_bf16_peak": 100 * fwd_tflops / BF16_PEAK_TFLOPS},
-             "qup_bwd_dsv3": {"ms": bwd_ms, "tflops": flops_bwd / (bwd_ms * 1e-3) / 1e12}}
+                                   "pct_bf16_peak": 100 * fwd_tflops / BF16_PEAK_TFLOPS, **pct(fwd_each)},
+             "qup_bwd_dsv3": {"ms": bwd_ms, "tflops": flops_bwd / (bwd_ms * 1e-3) / 1e12,
+                              "events_mean_ms": float(np.mean(bwd_each)), **pct(bwd_each)}}
     R = args.legs_reps
     # MXFP8 projection path, T = 8192 (2 x 4096)
     w2 = syn.workload("dsv3_fwd_mxfp8w")
