@@ -41,15 +41,6 @@ namespace {
 constexpr int TILE_T = 128;
 constexpr int TILE_N = 192;                // one DeepSeek-V3 head (D = 192)
 constexpr int NTHREADS = 256;
-constexpr int ROWB = 64;                  // bytes of one tile row per stage
-constexpr int XSB = TILE_T * ROWB;        // X part of a stage (8 KB)
-constexpr int WSB = TILE_N * ROWB;        // W part of a stage (12 KB)
-constexpr int SB = XSB + WSB;             // one ring slot (28 KB)
-constexpr int STAGES_BF16 = 4;            // ring slots: 80 KB per workgroup
-constexpr int STAGES_MX = 3;              // 60 KB + 20 KB of operand scales
-constexpr int LQX = XSB / 1024 / 4;       // X DMA loads per wave per stage (1 KB each)
-constexpr int LQW = WSB / 1024 / 4;       // W DMA loads per wave per stage
-constexpr int LPS = LQX + LQW;            // DMA loads per wave per stage
 constexpr int WBLK_N = 3;                 // 32-row blocks of N per wave (96 rows)
 constexpr int WBLK_T = 2;                 // 32-token blocks per wave (64 tokens)
 constexpr int WAVES_N = TILE_N / (32 * WBLK_N);  // waves along N (2); along T: 2
@@ -60,11 +51,39 @@ constexpr int MAX_KBLOCKS = 64;           // MXFP8: K <= 2048 (operand scales of
 constexpr int XSC_BYTES = TILE_T * MAX_KBLOCKS;
 constexpr int WSC_BYTES = TILE_N * MAX_KBLOCKS;
 
-// Chunk swizzle of a 64-byte row (four 16-byte chunks): chunk c of row r is
-// stored at c ^ ((r >> 2) & 3), so that the 16 lanes of a fragment read that
-// hit 16 consecutive rows spread over all bank groups.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int roff(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
+enum { MODE_BF16 = 0, MODE_MX_EXACT = 1, MODE_MX_FP8 = 2, MODE_BF16_R64 = 3 };
+
+// Stage layout per mode: a ring slot holds ROWB bytes of each of the tile's
+// TILE_T X rows and TILE_N W rows. BF16 with K % 64 == 0 uses 128-byte row
+// slices (64 K-values, whole 128-byte lines per request) in a 2-slot ring;
+// BF16 with K % 64 == 32 uses 64-byte slices in 4 slots; E4M3 uses 64-byte
+// slices (64 K-values) in 3 slots plus the tile's operand scales. Every mode
+// takes 80 KB of LDS.
+template <int MODE>
+struct Tile {
+  static constexpr bool MX = MODE == MODE_MX_EXACT || MODE == MODE_MX_FP8;
+  static constexpr int ROWB = MODE == MODE_BF16 ? 128 : 64;
+  static constexpr int KPS = MX ? ROWB : ROWB / 2;  // K-values per stage
+  static constexpr int STAGES = MODE == MODE_BF16 ? 2 : (MX ? 3 : 4);
+  static constexpr int XSB = TILE_T * ROWB;         // X part of a slot
+  static constexpr int WSB = TILE_N * ROWB;         // W part of a slot
+  static constexpr int SB = XSB + WSB;
+  static constexpr int LQX = XSB / 4096;            // X DMA loads (1 KB) per wave per stage
+  static constexpr int LQW = WSB / 4096;
+  static constexpr int LPS = LQX + LQW;
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  static constexpr int RPL = 1024 / ROWB;           // rows per 1 KB wave load
+};
+
+// Chunk swizzle: 16-byte chunk c of row r is stored at c ^ swz(r), so the 16
+// lanes of one LDS pass of a fragment read (16 consecutive rows, one chunk)
+// hit distinct bank groups: (r >> 2) & 3 for 64-byte rows (four chunks),
+// (r >> 1) & 7 for 128-byte rows (eight chunks; odd rows sit in the other
+// half of the banks).
+template <int ROWB>
+__device__ __forceinline__ int swz(int r) { return ROWB == 64 ? (r >> 2) & 3 : (r >> 1) & 7; }
+template <int ROWB>
+__device__ __forceinline__ int roff(int r, int c) { return r * ROWB + ((c ^ swz<ROWB>(r)) << 4); }
 
 
 // ---------------------------------------------------------------------------
@@ -280,54 +299,53 @@ __device__ __forceinline__ void tile_coords(const TileGrid& g, int u, int& tt, i
   tn = w / rows;
 }
 
-enum { MODE_BF16 = 0, MODE_MX_EXACT = 1, MODE_MX_FP8 = 2 };
-
-template <int MODE>
-struct Tile {
-  static constexpr bool MX = MODE != MODE_BF16;
-  // K-values per stage: 32 bf16 or 64 E4M3 per 64-byte row slice
-  static constexpr int KPS = MX ? 64 : 32;
-};
 
 // Per-lane DMA source offsets of one tile (rows clamped into the matrix so
 // that partial tiles never read out of bounds; clamped rows only feed
-// accumulators the epilogue discards).
+// accumulators the epilogue discards). Wave load q of wave w fills rows
+// RPL (4q + w) .. +RPL-1 of the slot; lane i takes row i / CPR and the source
+// chunk whose swizzled place is chunk i % CPR.
+template <int MODE>
 struct DmaPlan {
-  uint32_t xo[LQX];
-  uint32_t wo[LQW];
+  uint32_t xo[Tile<MODE>::LQX];
+  uint32_t wo[Tile<MODE>::LQW];
 };
 
-__device__ __forceinline__ DmaPlan dma_plan(const FwdParams& p, int64_t t0, int n0, int wave, int lane,
-                                           int row_bytes) {
-  DmaPlan d;
-  const int lr = lane >> 2;
-  const int c = (lane & 3) ^ swz(lr);
+template <int MODE>
+__device__ __forceinline__ DmaPlan<MODE> dma_plan(const FwdParams& p, int64_t t0, int n0, int wave, int lane,
+                                                  int row_bytes) {
+  using TL = Tile<MODE>;
+  DmaPlan<MODE> d;
+  const int ci = lane % TL::CPR;
 #pragma unroll
-  for (int q = 0; q < LQX; ++q) {
-    int64_t t = t0 + 16 * (4 * q + wave) + lr;
+  for (int q = 0; q < TL::LQX; ++q) {
+    const int r = TL::RPL * (4 * q + wave) + lane / TL::CPR;
+    int64_t t = t0 + r;
     if (t >= p.T) t = p.T - 1;
-    d.xo[q] = (uint32_t)(t * row_bytes + c * 16);
+    d.xo[q] = (uint32_t)(t * row_bytes + ((ci ^ swz<TL::ROWB>(r)) << 4));
   }
 #pragma unroll
-  for (int q = 0; q < LQW; ++q) {
-    int n = n0 + 16 * (4 * q + wave) + lr;
+  for (int q = 0; q < TL::LQW; ++q) {
+    const int r = TL::RPL * (4 * q + wave) + lane / TL::CPR;
+    int n = n0 + r;
     if (n >= p.N) n = p.N - 1;
-    d.wo[q] = (uint32_t)((int64_t)n * row_bytes + c * 16);
+    d.wo[q] = (uint32_t)((int64_t)n * row_bytes + ((ci ^ swz<TL::ROWB>(r)) << 4));
   }
   return d;
 }
 
 // Stage `kt` of the tile (K slice kt, clamped to the last one) into ring
 // slot `slot_kt % STAGES`.
-template <int STAGES>
-__device__ __forceinline__ void issue_stage(const DmaPlan& d, const uint8_t* xb, const uint8_t* wb,
+template <int MODE>
+__device__ __forceinline__ void issue_stage(const DmaPlan<MODE>& d, const uint8_t* xb, const uint8_t* wb,
                                             int kt, int nk, int slot_kt, uint32_t ring, int wave) {
-  const uint32_t slot = ring + (uint32_t)(slot_kt % STAGES) * SB;
-  const int64_t kb = (int64_t)(kt < nk ? kt : nk - 1) * ROWB;
+  using TL = Tile<MODE>;
+  const uint32_t slot = ring + (uint32_t)(slot_kt % TL::STAGES) * TL::SB;
+  const int64_t kb = (int64_t)(kt < nk ? kt : nk - 1) * TL::ROWB;
 #pragma unroll
-  for (int q = 0; q < LQX; ++q) dma16(xb + kb, d.xo[q], slot + (4 * q + wave) * 1024);
+  for (int q = 0; q < TL::LQX; ++q) dma16(xb + kb, d.xo[q], slot + (4 * q + wave) * 1024);
 #pragma unroll
-  for (int q = 0; q < LQW; ++q) dma16(wb + kb, d.wo[q], slot + XSB + (4 * q + wave) * 1024);
+  for (int q = 0; q < TL::LQW; ++q) dma16(wb + kb, d.wo[q], slot + TL::XSB + (4 * q + wave) * 1024);
 }
 
 // Four E4M3 codes -> four bf16 (two dwords), each times 2^(scale - 127).
@@ -345,7 +363,7 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
 __device__ __forceinline__ void frag_mx_exact(const uint8_t* rowp, int c, int r, float scale, bf16x8_t& f0,
                                               bf16x8_t& f1) {
   // 16 codes of chunk c of this row slice -> two bf16x8 fragments
-  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rowp + ((c ^ swz(r)) << 4));
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rowp + ((c ^ swz<64>(r)) << 4));
   const u32x2_t q0 = cvt4(v[0], scale), q1 = cvt4(v[1], scale);
   const u32x2_t q2 = cvt4(v[2], scale), q3 = cvt4(v[3], scale);
   f0 = __builtin_bit_cast(bf16x8_t, u32x4_t{q0[0], q0[1], q1[0], q1[1]});
@@ -356,22 +374,24 @@ template <int MODE>
 __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const uint8_t* cur,
                                           const uint8_t* xsc, const uint8_t* wsc, int kblocks, int kt,
                                           int arow0, int brow0, int half) {
-  if (MODE == MODE_BF16) {
-    // all fragments of both k16 steps first, so the second step's LDS reads
-    // are in flight while the first step's MFMAs run
-    bf16x8_t a[2][WBLK_N], b[2][WBLK_T];
+  using TL = Tile<MODE>;
+  if (!TL::MX) {
+    // all fragments of the stage's k16 steps first, so the later steps' LDS
+    // reads are in flight while the first step's MFMAs run
+    constexpr int NJS = TL::KPS / 16;
+    bf16x8_t a[NJS][WBLK_N], b[NJS][WBLK_T];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJS; ++j) {
 #pragma unroll
       for (int nb = 0; nb < WBLK_N; ++nb)
-        a[j][nb] = *reinterpret_cast<const bf16x8_t*>(cur + XSB + roff(arow0 + 32 * nb, 2 * j + half));
+        a[j][nb] = *reinterpret_cast<const bf16x8_t*>(cur + TL::XSB + roff<TL::ROWB>(arow0 + 32 * nb, 2 * j + half));
 #pragma unroll
       for (int tb = 0; tb < WBLK_T; ++tb)
-        b[j][tb] = *reinterpret_cast<const bf16x8_t*>(cur + roff(brow0 + 32 * tb, 2 * j + half));
+        b[j][tb] = *reinterpret_cast<const bf16x8_t*>(cur + roff<TL::ROWB>(brow0 + 32 * tb, 2 * j + half));
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead (see comment above)
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJS; ++j)
 #pragma unroll
       for (int tb = 0; tb < WBLK_T; ++tb)
 #pragma unroll
@@ -391,12 +411,12 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
 #pragma unroll
       for (int nb = 0; nb < WBLK_N; ++nb) {
         const int r = arow0 + 32 * nb;
-        frag_mx_exact(cur + XSB + r * ROWB, c, r, e8m0_to_f32(wsc[kblk * TILE_N + r]), a0[nb], a1[nb]);
+        frag_mx_exact(cur + TL::XSB + r * TL::ROWB, c, r, e8m0_to_f32(wsc[kblk * TILE_N + r]), a0[nb], a1[nb]);
       }
 #pragma unroll
       for (int tb = 0; tb < WBLK_T; ++tb) {
         const int r = brow0 + 32 * tb;
-        frag_mx_exact(cur + r * ROWB, c, r, e8m0_to_f32(xsc[kblk * TILE_T + r]), b0[tb], b1[tb]);
+        frag_mx_exact(cur + r * TL::ROWB, c, r, e8m0_to_f32(xsc[kblk * TILE_T + r]), b0[tb], b1[tb]);
       }
 #pragma unroll
       for (int nb = 0; nb < WBLK_N; ++nb)
@@ -420,8 +440,8 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
 #pragma unroll
     for (int nb = 0; nb < WBLK_N; ++nb) {
       const int r = arow0 + 32 * nb;
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + XSB + roff(r, half));
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + XSB + roff(r, 2 + half));
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + TL::XSB + roff<64>(r, half));
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + TL::XSB + roff<64>(r, 2 + half));
       a[nb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       sa[nb] = wsc[kblk * TILE_N + r];
@@ -429,8 +449,8 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
 #pragma unroll
     for (int tb = 0; tb < WBLK_T; ++tb) {
       const int r = brow0 + 32 * tb;
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + roff(r, half));
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + roff(r, 2 + half));
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + roff<64>(r, half));
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + roff<64>(r, 2 + half));
       b[tb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       sb[tb] = xsc[kblk * TILE_T + r];
@@ -468,10 +488,11 @@ __device__ __forceinline__ void load_tile_scales(const FwdParams& p, int64_t t0,
 template <int MODE>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(WG_PER_CU, WG_PER_CU)))
 void qup_fwd_kernel(FwdParams p) {
-  constexpr bool MX = Tile<MODE>::MX;
-  constexpr int KPS = Tile<MODE>::KPS;
-  constexpr int STAGES = MX ? STAGES_MX : STAGES_BF16;
-  constexpr int RING = SB * STAGES;
+  using TL = Tile<MODE>;
+  constexpr bool MX = TL::MX;
+  constexpr int KPS = TL::KPS;
+  constexpr int STAGES = TL::STAGES;
+  constexpr int RING = TL::SB * STAGES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[RING + (MX ? XSC_BYTES + WSC_BYTES : 0)];
   uint8_t* xsc = lds + RING;
   uint8_t* wsc = xsc + XSC_BYTES;
@@ -500,13 +521,13 @@ void qup_fwd_kernel(FwdParams p) {
   tile_coords(g, u, tt, tn);
   int64_t t0 = (int64_t)tt * TILE_T;
   int n0 = tn * TILE_N;
-  DmaPlan dp = dma_plan(p, t0, n0, wave, lane, row_bytes);
+  DmaPlan<MODE> dp = dma_plan<MODE>(p, t0, n0, wave, lane, row_bytes);
   if (MX) {
     load_tile_scales(p, t0, n0, xsc, wsc, tid);
     __syncthreads();
   }
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue_stage<STAGES>(dp, xb, wb, s, nk, s, ring, wave);
+  for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, s, ring, wave);
 
   for (;;) {
     f32x16_t acc[WBLK_N][WBLK_T];
@@ -518,14 +539,14 @@ void qup_fwd_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     for (int kt = 0; kt < nk; ++kt) {
-      vm_wait<(STAGES - 2) * LPS>();
+      vm_wait<(STAGES - 2) * TL::LPS>();
       barrier();
       // Always issue (past the last stage the source clamps to it) so every
       // iteration has the same number of loads in flight; slot
       // (kt + STAGES - 1) % STAGES was read in iteration kt - 1 and every
       // wave has passed the barrier since.
-      issue_stage<STAGES>(dp, xb, wb, kt + STAGES - 1, nk, kt + STAGES - 1, ring, wave);
-      mma_stage<MODE>(acc, lds + (kt % STAGES) * SB, xsc, wsc, kblocks, kt, arow0, brow0, half);
+      issue_stage<MODE>(dp, xb, wb, kt + STAGES - 1, nk, kt + STAGES - 1, ring, wave);
+      mma_stage<MODE>(acc, lds + (kt % STAGES) * TL::SB, xsc, wsc, kblocks, kt, arow0, brow0, half);
     }
 
     // Next tile of this workgroup: start its first stages before the
@@ -540,9 +561,9 @@ void qup_fwd_kernel(FwdParams p) {
       tile_coords(g, un, tt, tn);
       t0 = (int64_t)tt * TILE_T;
       n0 = tn * TILE_N;
-      dp = dma_plan(p, t0, n0, wave, lane, row_bytes);
+      dp = dma_plan<MODE>(p, t0, n0, wave, lane, row_bytes);
 #pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s) issue_stage<STAGES>(dp, xb, wb, s, nk, s, ring, wave);
+      for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, s, ring, wave);
     }
     epilogue_tile(p, tm, acc, n0c + 32 * WBLK_N * wn, t0c + 32 * WBLK_T * wt + (lane & 31), lane);
     if (!more) break;
@@ -569,8 +590,11 @@ int fwd_grid(const FwdParams& p, int num_cus) {
 bool fwd_scales_fit(int K) { return K / 32 <= MAX_KBLOCKS; }
 
 hipError_t launch_qup_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(qup_fwd_kernel<MODE_BF16>, dim3(fwd_grid(p, device_cu_count())), dim3(NTHREADS), 0,
-                     stream, p);
+  const dim3 grid(fwd_grid(p, device_cu_count()));
+  if (p.K % 64 == 0)
+    hipLaunchKernelGGL(qup_fwd_kernel<MODE_BF16>, grid, dim3(NTHREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL(qup_fwd_kernel<MODE_BF16_R64>, grid, dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
