@@ -181,21 +181,36 @@ __global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict_
 // ---------------------------------------------------------------------------
 constexpr int BG_TI = 192;
 constexpr int BG_TJ = 128;
-constexpr int BG_KS = 32;
 constexpr int BG_THREADS = 256;
-constexpr int BG_STAGES = 4;
 constexpr int BG_WG_PER_CU = 2;
 constexpr int BG_RPP = BG_TI * 2;          // P row pitch (MN-major), bytes
 constexpr int BG_RPQ = BG_TJ * 2;          // Q row pitch when MN-major
-constexpr int BG_PB = BG_KS * BG_RPP;      // P part of a stage (12 KB)
-constexpr int BG_QB = BG_KS * BG_RPQ;      // Q part (8 KB, either layout)
-constexpr int BG_SB = BG_PB + BG_QB;
-constexpr int BG_LP = BG_PB / 4096;        // P DMA loads per wave per stage
-constexpr int BG_LQ = BG_QB / 4096;
-constexpr int BG_LPS = BG_LP + BG_LQ;
 constexpr int BG_BI = BG_TI / 64;          // 32-blocks of i per wave (2 waves along i)
 constexpr int BG_BJ = BG_TJ / 64;          // 32-blocks of j per wave
-static_assert(BG_PB % 4096 == 0 && BG_QB % 4096 == 0, "whole DMA rounds per stage");
+
+// Stage layout for KS reduction values per stage. KS = 32: 4 ring slots of
+// 20 KB; KS = 64 (a K-major Q then arrives as whole 128-byte lines per row):
+// 2 slots of 40 KB. Both take 80 KB of LDS.
+template <int KS>
+struct Bg {
+  static constexpr int STAGES = KS == 64 ? 2 : 4;
+  static constexpr int PB = KS * BG_RPP;     // P part of a slot
+  static constexpr int QB = KS * BG_RPQ;     // Q part (MN-major KS rows, or K-major TJ rows x 2 KS bytes)
+  static constexpr int SB = PB + QB;
+  static constexpr int LP = PB / 4096;       // P DMA loads (1 KB) per wave per stage
+  static constexpr int LQ = QB / 4096;
+  static constexpr int LPS = LP + LQ;
+  static constexpr int NJS = KS / 16;        // k16 MFMA steps per stage
+  static constexpr int QROWB = 2 * KS;       // K-major Q: bytes of a row per stage
+  static constexpr int QCPR = QROWB / 16;    // its 16-byte chunks
+  static constexpr int QRPL = 1024 / QROWB;  // its rows per 1 KB wave load
+  static_assert(PB % 4096 == 0 && QB % 4096 == 0, "whole DMA rounds per stage");
+};
+
+// K-major chunk swizzle (as in the forward): 64-byte rows c ^ ((r >> 2) & 3),
+// 128-byte rows c ^ ((r >> 1) & 7).
+template <int ROWB>
+__device__ __forceinline__ int k_swz(int r) { return ROWB == 64 ? (r >> 2) & 3 : (r >> 1) & 7; }
 
 template <int RP>
 __device__ __forceinline__ int mn_swz(int r) {
@@ -230,11 +245,12 @@ __device__ __forceinline__ void bg_coords(const BgGrid& g, int u, int& z, int& t
 }
 
 // Per-lane DMA sources of one tile (independent of the stage).
+template <int KS>
 struct BgDma {
-  int pr[BG_LP];       // P: stage row
-  uint32_t pc[BG_LP];  // P: byte offset inside the row (tile column base included)
-  int qr[BG_LQ];       // Q MN-major: stage row; K-major: unused
-  uint32_t qc[BG_LQ];  // Q MN-major: byte offset in row; K-major: row offset + chunk
+  int pr[Bg<KS>::LP];       // P: stage row
+  uint32_t pc[Bg<KS>::LP];  // P: byte offset inside the row (tile column base included)
+  int qr[Bg<KS>::LQ];       // Q MN-major: stage row; K-major: unused
+  uint32_t qc[Bg<KS>::LQ];  // Q MN-major: byte offset in row; K-major: row offset + chunk
 };
 
 // Chunk e (16 bytes) of an MN-major stage of `COLS` columns: its stage row
@@ -251,16 +267,17 @@ __device__ __forceinline__ void mn_src(int e, int col0, int cols, int& row, uint
   off = (uint32_t)((col0 + gc * 8) * 2);
 }
 
-template <bool QK>
-__device__ __forceinline__ BgDma bg_dma(const BGemm& g, int i0, int j0, int wave, int lane) {
-  BgDma d;
+template <bool QK, int KS>
+__device__ __forceinline__ BgDma<KS> bg_dma(const BGemm& g, int i0, int j0, int wave, int lane) {
+  using B = Bg<KS>;
+  BgDma<KS> d;
 #pragma unroll
-  for (int q = 0; q < BG_LP; ++q) mn_src<BG_TI>((4 * q + wave) * 64 + lane, i0, g.I, d.pr[q], d.pc[q]);
+  for (int q = 0; q < B::LP; ++q) mn_src<BG_TI>((4 * q + wave) * 64 + lane, i0, g.I, d.pr[q], d.pc[q]);
   if (QK) {
 #pragma unroll
-    for (int q = 0; q < BG_LQ; ++q) {
-      const int row = 16 * (4 * q + wave) + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
+    for (int q = 0; q < B::LQ; ++q) {
+      const int row = B::QRPL * (4 * q + wave) + lane / B::QCPR;
+      const int c = (lane % B::QCPR) ^ k_swz<B::QROWB>(row);
       int j = j0 + row;
       if (j >= g.J) j = g.J - 1;
       d.qr[q] = 0;
@@ -268,31 +285,32 @@ __device__ __forceinline__ BgDma bg_dma(const BGemm& g, int i0, int j0, int wave
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < BG_LQ; ++q) mn_src<BG_TJ>((4 * q + wave) * 64 + lane, j0, g.J, d.qr[q], d.qc[q]);
+    for (int q = 0; q < B::LQ; ++q) mn_src<BG_TJ>((4 * q + wave) * 64 + lane, j0, g.J, d.qr[q], d.qc[q]);
   }
   return d;
 }
 
 // Stage whose reduction rows start at rs (rows past rlim are clamped to it)
 // into the ring slot at LDS address `slot`.
-template <bool QK>
-__device__ __forceinline__ void bg_issue(const BGemm& g, const BgDma& d, const uint8_t* qtile, int64_t rs,
+template <bool QK, int KS>
+__device__ __forceinline__ void bg_issue(const BGemm& g, const BgDma<KS>& d, const uint8_t* qtile, int64_t rs,
                                          int rlim, uint32_t slot, int wave) {
+  using B = Bg<KS>;
   const uint8_t* ps = g.p + rs * g.ldp;
   const uint32_t ldp = (uint32_t)g.ldp;
 #pragma unroll
-  for (int q = 0; q < BG_LP; ++q)
+  for (int q = 0; q < B::LP; ++q)
     dma16(ps, (uint32_t)min(d.pr[q], rlim) * ldp + d.pc[q], slot + (4 * q + wave) * 1024);
   if (QK) {
     const uint8_t* qs = qtile + rs * 2;
 #pragma unroll
-    for (int q = 0; q < BG_LQ; ++q) dma16(qs, d.qc[q], slot + BG_PB + (4 * q + wave) * 1024);
+    for (int q = 0; q < B::LQ; ++q) dma16(qs, d.qc[q], slot + B::PB + (4 * q + wave) * 1024);
   } else {
     const uint8_t* qs = g.q + rs * g.ldq;
     const uint32_t ldq = (uint32_t)g.ldq;
 #pragma unroll
-    for (int q = 0; q < BG_LQ; ++q)
-      dma16(qs, (uint32_t)min(d.qr[q], rlim) * ldq + d.qc[q], slot + BG_PB + (4 * q + wave) * 1024);
+    for (int q = 0; q < B::LQ; ++q)
+      dma16(qs, (uint32_t)min(d.qr[q], rlim) * ldq + d.qc[q], slot + B::PB + (4 * q + wave) * 1024);
   }
 }
 
@@ -328,8 +346,9 @@ struct BgFrag {
   uint32_t q[BG_BJ];  // Q block jb
 };
 
-template <bool QK>
+template <bool QK, int KS>
 __device__ __forceinline__ BgFrag bg_frag(int wi, int wj, int lane) {
+  using B = Bg<KS>;
   BgFrag f;
   const int g = lane >> 4, s = lane & 15;
   const int rsub = 8 * (g >> 1) + (s >> 2);         // row inside a 16-row step
@@ -341,27 +360,29 @@ __device__ __forceinline__ BgFrag bg_frag(int wi, int wj, int lane) {
   for (int jb = 0; jb < BG_BJ; ++jb) {
     if (QK) {
       const int row = 64 * wj + 32 * jb + (lane & 31);
-      f.q[jb] = BG_PB + row * 64;  // chunk added per step
+      f.q[jb] = B::PB + row * B::QROWB;  // chunk added per step
     } else {
-      f.q[jb] = BG_PB + rsub * BG_RPQ + (((BG_BJ * wj + jb) ^ mn_swz<BG_RPQ>(rsub)) << 6) + cin;
+      f.q[jb] = B::PB + rsub * BG_RPQ + (((BG_BJ * wj + jb) ^ mn_swz<BG_RPQ>(rsub)) << 6) + cin;
     }
   }
   return f;
 }
 
-template <bool QK, bool TAIL>
+template <bool QK, int KS, bool TAIL>
 __device__ __forceinline__ void bg_mma(f32x16_t (&acc)[BG_BI][BG_BJ], uint32_t cur, const BgFrag& f, int lane,
                                        int rem) {
+  using B = Bg<KS>;
   const int half = lane >> 5;
-  bf16x8_t a[2][BG_BI], b[2][BG_BJ];
+  bf16x8_t a[B::NJS][BG_BI], b[B::NJS][BG_BJ];
 #pragma unroll
-  for (int js = 0; js < 2; ++js) {
+  for (int js = 0; js < B::NJS; ++js) {
 #pragma unroll
     for (int ib = 0; ib < BG_BI; ++ib) a[js][ib] = tr_frag(cur + f.p[ib] + 16 * js * BG_RPP, BG_RPP);
 #pragma unroll
     for (int jb = 0; jb < BG_BJ; ++jb) {
       if (QK) {
-        const int c = (2 * js + half) ^ (((lane & 31) >> 2) & 3);
+        // fragment rows 64 wj + 32 jb + lane%32: the swizzle key is lane%32's
+        const int c = (2 * js + half) ^ k_swz<B::QROWB>(lane & 31);
         b[js][jb] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
             (uintptr_t)(cur + f.q[jb] + (c << 4)));
       } else {
@@ -369,13 +390,13 @@ __device__ __forceinline__ void bg_mma(f32x16_t (&acc)[BG_BI][BG_BJ], uint32_t c
       }
     }
   }
-  // keep every fragment read of the stage ahead of its MFMAs: the second
-  // k16 step's reads then complete under the first step's MFMAs (the default
+  // keep every fragment read of the stage ahead of its MFMAs: the later k16
+  // steps' reads then complete under the first step's MFMAs (the default
   // schedule interleaves each read right before its use)
   __builtin_amdgcn_sched_barrier(0);
   if (TAIL) {
 #pragma unroll
-    for (int js = 0; js < 2; ++js) {
+    for (int js = 0; js < B::NJS; ++js) {
       const int kb = 16 * js + 8 * half;
 #pragma unroll
       for (int ib = 0; ib < BG_BI; ++ib) a[js][ib] = mask_tail(a[js][ib], kb, rem);
@@ -386,7 +407,7 @@ __device__ __forceinline__ void bg_mma(f32x16_t (&acc)[BG_BI][BG_BJ], uint32_t c
     }
   }
 #pragma unroll
-  for (int js = 0; js < 2; ++js)
+  for (int js = 0; js < B::NJS; ++js)
 #pragma unroll
     for (int jb = 0; jb < BG_BJ; ++jb)
 #pragma unroll
@@ -440,10 +461,11 @@ __device__ __forceinline__ void bg_store(const BGemm& g, const f32x16_t (&acc)[B
   }
 }
 
-template <bool QK, bool F32>
+template <bool QK, int KS, bool F32>
 __global__ __launch_bounds__(BG_THREADS) __attribute__((amdgpu_waves_per_eu(BG_WG_PER_CU, BG_WG_PER_CU)))
 void bgemm_kernel(BGemm g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[BG_STAGES * BG_SB];
+  using B = Bg<KS>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[B::STAGES * B::SB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -455,29 +477,29 @@ void bgemm_kernel(BGemm g) {
   gr.tj = (g.J + BG_TJ - 1) / BG_TJ;
   gr.per = gr.ti * gr.tj;
   gr.total = gr.per * g.splits;
-  const BgFrag fr = bg_frag<QK>(wi, wj, lane);
+  const BgFrag fr = bg_frag<QK, KS>(wi, wj, lane);
 
   int u = blockIdx.x;
   if (u >= gr.total) return;
   int z, ti, tj;
   bg_coords(gr, u, z, ti, tj);
   int i0 = ti * BG_TI, j0 = tj * BG_TJ;
-  int64_t r0 = (int64_t)z * g.sps * BG_KS;
-  int64_t r1 = min(g.R, r0 + (int64_t)g.sps * BG_KS);
-  int nk = (int)((r1 - r0 + BG_KS - 1) / BG_KS);
-  BgDma dp = bg_dma<QK>(g, i0, j0, wave, lane);
+  int64_t r0 = (int64_t)z * g.sps * KS;
+  int64_t r1 = min(g.R, r0 + (int64_t)g.sps * KS);
+  int nk = (int)((r1 - r0 + KS - 1) / KS);
+  BgDma<KS> dp = bg_dma<QK, KS>(g, i0, j0, wave, lane);
   const uint8_t* qt = g.q + (int64_t)j0 * g.ldq;  // K-major Q: the tile's first row
 
   // stage kt of the current tile (clamped to the last one) into slot s
   auto issue = [&](int kt, int slot_kt) {
     const int k = kt < nk ? kt : nk - 1;
-    const int64_t rs = r0 + (int64_t)k * BG_KS;
-    const int rlim = (int)min((int64_t)(BG_KS - 1), r1 - 1 - rs);
-    bg_issue<QK>(g, dp, qt, rs, rlim, ring + (uint32_t)(slot_kt % BG_STAGES) * BG_SB, wave);
+    const int64_t rs = r0 + (int64_t)k * KS;
+    const int rlim = (int)min((int64_t)(KS - 1), r1 - 1 - rs);
+    bg_issue<QK, KS>(g, dp, qt, rs, rlim, ring + (uint32_t)(slot_kt % B::STAGES) * B::SB, wave);
   };
 
 #pragma unroll
-  for (int s = 0; s < BG_STAGES - 1; ++s) issue(s, s);
+  for (int s = 0; s < B::STAGES - 1; ++s) issue(s, s);
 
   for (;;) {
     f32x16_t acc[BG_BI][BG_BJ];
@@ -488,23 +510,23 @@ void bgemm_kernel(BGemm g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    const int rem = (int)(r1 - r0 - (int64_t)(nk - 1) * BG_KS);  // rows of the last stage
-    const int nfull = rem == BG_KS ? nk : nk - 1;
+    const int rem = (int)(r1 - r0 - (int64_t)(nk - 1) * KS);  // rows of the last stage
+    const int nfull = rem == KS ? nk : nk - 1;
     // Full stages in a loop with one code path (a second MFMA path inside the
     // loop makes the compiler copy every accumulator at the merge).
     for (int kt = 0; kt < nfull; ++kt) {
-      vm_wait<(BG_STAGES - 2) * BG_LPS>();
+      vm_wait<(B::STAGES - 2) * B::LPS>();
       barrier();
       // slot (kt + STAGES - 1) % STAGES was read in iteration kt - 1, and every
       // wave has passed the barrier since
-      issue(kt + BG_STAGES - 1, kt + BG_STAGES - 1);
-      bg_mma<QK, false>(acc, ring + (uint32_t)(kt % BG_STAGES) * BG_SB, fr, lane, BG_KS);
+      issue(kt + B::STAGES - 1, kt + B::STAGES - 1);
+      bg_mma<QK, KS, false>(acc, ring + (uint32_t)(kt % B::STAGES) * B::SB, fr, lane, KS);
     }
     if (nfull < nk) {
       // partial last stage: no further stage to issue (the wait below drains all)
-      vm_wait<(BG_STAGES - 2) * BG_LPS>();
+      vm_wait<(B::STAGES - 2) * B::LPS>();
       barrier();
-      bg_mma<QK, true>(acc, ring + (uint32_t)(nfull % BG_STAGES) * BG_SB, fr, lane, rem);
+      bg_mma<QK, KS, true>(acc, ring + (uint32_t)(nfull % B::STAGES) * B::SB, fr, lane, rem);
     }
 
     // drain this tile's DMA (including the clamped stages issued past its
@@ -518,13 +540,13 @@ void bgemm_kernel(BGemm g) {
     bg_coords(gr, u, z, ti, tj);
     i0 = ti * BG_TI;
     j0 = tj * BG_TJ;
-    r0 = (int64_t)z * g.sps * BG_KS;
-    r1 = min(g.R, r0 + (int64_t)g.sps * BG_KS);
-    nk = (int)((r1 - r0 + BG_KS - 1) / BG_KS);
-    dp = bg_dma<QK>(g, i0, j0, wave, lane);
+    r0 = (int64_t)z * g.sps * KS;
+    r1 = min(g.R, r0 + (int64_t)g.sps * KS);
+    nk = (int)((r1 - r0 + KS - 1) / KS);
+    dp = bg_dma<QK, KS>(g, i0, j0, wave, lane);
     qt = g.q + (int64_t)j0 * g.ldq;
 #pragma unroll
-    for (int s = 0; s < BG_STAGES - 1; ++s) issue(s, s);
+    for (int s = 0; s < B::STAGES - 1; ++s) issue(s, s);
   }
 }
 
@@ -570,9 +592,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // resident workgroups cover the work in the least time, ceil(tiles s / slots)
 // rounds of ceil(stages / s) stages, preferring fewer splits (each split adds
 // an fp32 partial of dX to write and reduce) and at least 8 stages per split.
+// Reduction values per stage of the dX GEMM: 64 (whole 128-byte lines of
+// dq_pre per row) when N allows it.
+static int dx_stage_depth(int N) { return N % 64 == 0 ? 64 : 32; }
+
 static int dx_split_count(int64_t T, int N, int K) {
   const int64_t tiles = ((T + BG_TJ - 1) / BG_TJ) * ((K + BG_TI - 1) / BG_TI);
-  const int64_t stages = (N + BG_KS - 1) / BG_KS;
+  const int64_t stages = N / dx_stage_depth(N);
   const int cus = device_cu_count();
   const int64_t slots = (int64_t)(cus > 0 ? cus : 256) * BG_WG_PER_CU;
   int best = 1;
@@ -634,15 +660,20 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     g.I = p.K;
     g.J = (int)p.T;
     g.R = p.N;
-    const int stages = (p.N + BG_KS - 1) / BG_KS;
+    const int ks = dx_stage_depth(p.N);
+    const int stages = p.N / ks;
     g.splits = pl.dx_splits;
     g.sps = (stages + g.splits - 1) / g.splits;
     const bool split = g.splits > 1;
     g.out = split ? static_cast<void*>(ws + pl.dx_off) : static_cast<void*>(p.dx);
-    if (split)
-      hipLaunchKernelGGL((bgemm_kernel<true, true>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
-    else
-      hipLaunchKernelGGL((bgemm_kernel<true, false>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
+    const dim3 grid(bg_grid(g, cus));
+    if (ks == 64) {
+      if (split) hipLaunchKernelGGL((bgemm_kernel<true, 64, true>), grid, dim3(BG_THREADS), 0, stream, g);
+      else hipLaunchKernelGGL((bgemm_kernel<true, 64, false>), grid, dim3(BG_THREADS), 0, stream, g);
+    } else {
+      if (split) hipLaunchKernelGGL((bgemm_kernel<true, 32, true>), grid, dim3(BG_THREADS), 0, stream, g);
+      else hipLaunchKernelGGL((bgemm_kernel<true, 32, false>), grid, dim3(BG_THREADS), 0, stream, g);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (split) {
@@ -664,12 +695,12 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     g.J = p.N;
     g.R = p.T;
     g.splits = 1;
-    g.sps = (int)((p.T + BG_KS - 1) / BG_KS);
+    g.sps = (int)((p.T + 31) / 32);  // stages of 32 tokens (both operands arrive as long rows)
     g.out = p.dw;
     if (p.dw_fp32)
-      hipLaunchKernelGGL((bgemm_kernel<false, true>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
+      hipLaunchKernelGGL((bgemm_kernel<false, 32, true>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
     else
-      hipLaunchKernelGGL((bgemm_kernel<false, false>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
+      hipLaunchKernelGGL((bgemm_kernel<false, 32, false>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -375,6 +375,20 @@ def test_bwd_dx_only_and_dw_only():
             assert frob_rel(o.to_f64(dw.cpu()), r.dw) <= 1e-2
 
 
+def test_bwd_width_not_multiple_of_64():
+    """N = 96 (3 heads x 16+16): the dX reduction runs in 32-value stages."""
+    T, K, H = 150, 96, 3
+    x = syn.normal_bf16((T, K), 1.0, 90)
+    w = syn.normal_bf16((H * 32, K), 0.1, 91)
+    dq = syn.normal_bf16((T, H, 32), 1e-2, 92)
+    g = run_bwd(dq, x, w, H=H, dn=16, dr=16, S=T)
+    r = o.qup_backward(dq, x, w, H=H, d_nope=16, d_rope=16, cos=g["oc"], sin=g["os"], S=T)
+    check_bf16(bits16(g["dq_pre"]), o.f32_to_bf16_bits(r.dq_pre.astype(np.float32)), "dq_pre")
+    assert frob_rel(o.to_f64(g["dx"].cpu()), r.dx) <= 1e-2
+    assert frob_rel(o.to_f64(g["dw"].cpu()), r.dw) <= 1e-2
+    assert frob_rel(o.to_f64(g["db"].cpu()), r.db) <= 1e-2
+
+
 def test_bwd_zero_tokens_zeroes_dw_db():
     K, H = 64, 2
     x = torch.empty(0, K, dtype=torch.bfloat16, device=DEV)
