@@ -695,12 +695,12 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     g.J = p.N;
     g.R = p.T;
     g.splits = 1;
-    g.sps = (int)((p.T + 31) / 32);  // stages of 32 tokens (both operands arrive as long rows)
+    g.sps = (int)((p.T + 63) / 64);
     g.out = p.dw;
     if (p.dw_fp32)
-      hipLaunchKernelGGL((bgemm_kernel<false, 32, true>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
+      hipLaunchKernelGGL((bgemm_kernel<false, 64, true>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
     else
-      hipLaunchKernelGGL((bgemm_kernel<false, 32, false>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
+      hipLaunchKernelGGL((bgemm_kernel<false, 64, false>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
