@@ -204,13 +204,22 @@ def test_fwd_mxfp8_projection_small():
     full_compare_fwd(x, w, H=H, dn=128, dr=64, B=1, S=T, mx_in=True)
 
 
-@pytest.mark.parametrize("fp8_mfma", [False, True])
-def test_fwd_mxfp8_operands_narrow_codes_random_scales(fp8_mfma):
+def test_fwd_mxfp8_projection_largest_k():
+    """K = 2048, the largest K whose operand scales fit the forward tile's LDS
+    scale area (64 blocks per row); ragged token tile."""
+    T, K, H = 96, 2048, 2
+    x = syn.normal_bf16((T, K), 1.0, 44)
+    w = syn.normal_bf16((H * 192, K), 0.02, 45)
+    full_compare_fwd(x, w, H=H, dn=128, dr=64, B=1, S=T, mx_in=True)
+
+
+@pytest.mark.parametrize("fp8_mfma,K", [(False, 512), (True, 512), (False, 2048), (True, 2048)])
+def test_fwd_mxfp8_operands_narrow_codes_random_scales(fp8_mfma, K):
     """MXFP8 X and W given directly: every code has exponent field 7 (values
     +-1..1.875), scales vary per 32-block. Products then never differ by more
     than 2^4, so the result is exact up to fp32 summation: this isolates the
     operand/scale layout of the scaled MFMA from its dot-product precision."""
-    T, K, H, D = 256, 512, 2, 192
+    T, H, D = 256, 2, 192
     rng = np.random.default_rng(80)
     def codes(shape):
         return ((rng.integers(0, 2, shape) << 7) | (7 << 3) | rng.integers(0, 8, shape)).astype(np.uint8)
@@ -383,6 +392,22 @@ def test_bwd_width_not_multiple_of_64():
     dq = syn.normal_bf16((T, H, 32), 1e-2, 92)
     g = run_bwd(dq, x, w, H=H, dn=16, dr=16, S=T)
     r = o.qup_backward(dq, x, w, H=H, d_nope=16, d_rope=16, cos=g["oc"], sin=g["os"], S=T)
+    check_bf16(bits16(g["dq_pre"]), o.f32_to_bf16_bits(r.dq_pre.astype(np.float32)), "dq_pre")
+    assert frob_rel(o.to_f64(g["dx"].cpu()), r.dx) <= 1e-2
+    assert frob_rel(o.to_f64(g["dw"].cpu()), r.dw) <= 1e-2
+    assert frob_rel(o.to_f64(g["db"].cpu()), r.db) <= 1e-2
+
+
+def test_bwd_sbhd():
+    """SBHD token order (t = s*B + b): positions s for the inverse rotation."""
+    B, S, K, H = 3, 77, 128, 2
+    T = B * S
+    x = syn.normal_bf16((T, K), 1.0, 95)
+    w = syn.normal_bf16((H * 192, K), 0.02, 96)
+    dq = syn.normal_bf16((T, H, 192), 1e-3, 97)
+    g = run_bwd(dq, x, w, H=H, dn=128, dr=64, fmt=m.FMT_SBHD, B=B, S=S)
+    r = o.qup_backward(dq, x, w, H=H, d_nope=128, d_rope=64, cos=g["oc"], sin=g["os"],
+                       fmt=o.FMT_SBHD, B=B, S=S)
     check_bf16(bits16(g["dq_pre"]), o.f32_to_bf16_bits(r.dq_pre.astype(np.float32)), "dq_pre")
     assert frob_rel(o.to_f64(g["dx"].cpu()), r.dx) <= 1e-2
     assert frob_rel(o.to_f64(g["dw"].cpu()), r.dw) <= 1e-2
