@@ -147,10 +147,10 @@ MLA_API mla_status mxfp8_quantize(const void* x, int32_t x_dtype, int64_t rows, 
  * 16-bit rounding. */
 typedef struct {
   const void* x;            /* BF16 [T, K] or MXFP8 codes [T, K]; 16-B aligned */
-  const uint8_t* x_scales;  /* MXFP8: [T, K/32] E8M0; else NULL */
+  const uint8_t* x_scales;  /* MXFP8: [T, K/32] E8M0, 4-B aligned; else NULL */
   int32_t x_dtype;          /* MLA_DTYPE_BF16 or MLA_DTYPE_MXFP8 */
   const void* w;            /* BF16 [N, K] or MXFP8 codes [N, K]; 16-B aligned */
-  const uint8_t* w_scales;  /* MXFP8: [N, K/32]; else NULL */
+  const uint8_t* w_scales;  /* MXFP8: [N, K/32], 4-B aligned; else NULL */
   int32_t w_dtype;          /* must equal x_dtype */
   const void* bias;         /* bf16 [N] added before the rotation, or NULL */
   int32_t K;                /* q_lora_rank; > 0, multiple of 32 (MXFP8: of 128) */
@@ -176,7 +176,8 @@ typedef struct {
 enum { MLA_FWD_FP8_MFMA = 1 };
 
 /* Errors: MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EUNSUPPORTED
- * (x_dtype != w_dtype), MLA_EDEVICE. */
+ * (x_dtype != w_dtype, or X or W spanning more than 4 GiB: the kernel
+ * addresses their rows with 32-bit offsets), MLA_EDEVICE. */
 MLA_API mla_status mla_qup_fwd(const mla_qup_fwd_args* args, void* stream);
 
 /* Backward:

@@ -179,7 +179,6 @@ mla_status mla_qup_fwd(const mla_qup_fwd_args* a, void* stream) {
   const bool mx_in = a->x_dtype == MLA_DTYPE_MXFP8;
   const bool mx_out = a->out_dtype == MLA_DTYPE_MXFP8;
   if (mx_in && a->K % 128 != 0) return MLA_EINVAL;
-  if (mx_in && !mla::fwd_scales_fit(a->K)) return MLA_EUNSUPPORTED;
   if ((st = check_rope(a->rope, a->d_rope, max_pos))) return st;
   const int64_t T = a->tokens.T;
   if (T == 0) return MLA_OK;
@@ -188,6 +187,8 @@ mla_status mla_qup_fwd(const mla_qup_fwd_args* a, void* stream) {
   if (mx_out && a->out_scales == nullptr) return MLA_EINVAL;
   if (!aligned(a->x, 16) || !aligned(a->w, 16) || !aligned(a->out, 16)) return MLA_EINVAL;
   if (a->bias && !aligned(a->bias, 2)) return MLA_EINVAL;
+  // each lane loads four consecutive scale bytes of a row as one dword
+  if (mx_in && (!aligned(a->x_scales, 4) || !aligned(a->w_scales, 4))) return MLA_EINVAL;
 
   const int D = a->d_nope + a->d_rope;
   const int64_t N = (int64_t)a->H * D;

@@ -62,9 +62,6 @@ BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx);
 
 // Compute units of the current device (cached per device; 0 if unknown).
 int device_cu_count();
-// Forward limits: DMA source offsets are 32-bit, and the MXFP8 operand
-// scales of one tile must fit the kernel's LDS scale area.
-bool fwd_scales_fit(int K);
 
 hipError_t launch_rope_cache(float* cos, float* sin, int rows, int d_rope, double base,
                              const mla_yarn* yarn, hipStream_t stream);

@@ -47,24 +47,20 @@ constexpr int WAVES_N = TILE_N / (32 * WBLK_N);  // waves along N (2); along T: 
 static_assert(WAVES_N * (TILE_T / (32 * WBLK_T)) == NTHREADS / 64, "2 x 2 waves");
 static_assert(WBLK_N == 3, "packed scale stores below are written for 3 blocks per wave");
 constexpr int WG_PER_CU = 2;              // two independent workgroups per CU
-constexpr int MAX_KBLOCKS = 64;           // MXFP8: K <= 2048 (operand scales of a tile live in LDS)
-constexpr int XSC_BYTES = TILE_T * MAX_KBLOCKS;
-constexpr int WSC_BYTES = TILE_N * MAX_KBLOCKS;
 
 enum { MODE_BF16 = 0, MODE_MX_EXACT = 1, MODE_MX_FP8 = 2, MODE_BF16_R64 = 3 };
 
 // Stage layout per mode: a ring slot holds ROWB bytes of each of the tile's
-// TILE_T X rows and TILE_N W rows. BF16 with K % 64 == 0 uses 128-byte row
-// slices (64 K-values, whole 128-byte lines per request) in a 2-slot ring;
-// BF16 with K % 64 == 32 uses 64-byte slices in 4 slots; E4M3 uses 64-byte
-// slices (64 K-values) in 3 slots plus the tile's operand scales. Every mode
-// takes 80 KB of LDS.
+// TILE_T X rows and TILE_N W rows. 128-byte row slices (whole cache lines per
+// request: 64 bf16 or 128 E4M3 K-values) in a 2-slot ring, except BF16 with
+// K % 64 == 32, which uses 64-byte slices in 4 slots. Every mode takes 80 KB
+// of LDS; E4M3 operand scales travel in registers (see StageScales).
 template <int MODE>
 struct Tile {
   static constexpr bool MX = MODE == MODE_MX_EXACT || MODE == MODE_MX_FP8;
-  static constexpr int ROWB = MODE == MODE_BF16 ? 128 : 64;
+  static constexpr int ROWB = MODE == MODE_BF16_R64 ? 64 : 128;
   static constexpr int KPS = MX ? ROWB : ROWB / 2;  // K-values per stage
-  static constexpr int STAGES = MODE == MODE_BF16 ? 2 : (MX ? 3 : 4);
+  static constexpr int STAGES = MODE == MODE_BF16_R64 ? 4 : 2;
   static constexpr int XSB = TILE_T * ROWB;         // X part of a slot
   static constexpr int WSB = TILE_N * ROWB;         // W part of a slot
   static constexpr int SB = XSB + WSB;
@@ -362,18 +358,58 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
 
 __device__ __forceinline__ void frag_mx_exact(const uint8_t* rowp, int c, int r, float scale, bf16x8_t& f0,
                                               bf16x8_t& f1) {
-  // 16 codes of chunk c of this row slice -> two bf16x8 fragments
-  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rowp + ((c ^ swz<64>(r)) << 4));
+  // 16 codes of chunk c of this 128-byte row slice -> two bf16x8 fragments
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rowp + ((c ^ swz<128>(r)) << 4));
   const u32x2_t q0 = cvt4(v[0], scale), q1 = cvt4(v[1], scale);
   const u32x2_t q2 = cvt4(v[2], scale), q3 = cvt4(v[3], scale);
   f0 = __builtin_bit_cast(bf16x8_t, u32x4_t{q0[0], q0[1], q1[0], q1[1]});
   f1 = __builtin_bit_cast(bf16x8_t, u32x4_t{q2[0], q2[1], q3[0], q3[1]});
 }
 
+// MXFP8 operand scales of one stage for this lane's fragment rows: the four
+// E8M0 bytes of K blocks 4k .. 4k+3 of W rows arow0 + 32 nb and of X rows
+// brow0 + 32 tb, one aligned dword per row (K % 128 == 0), loaded with the
+// stage's DMA and consumed after the same wait.
+struct StageScales {
+  uint32_t w[WBLK_N];
+  uint32_t x[WBLK_T];
+};
+struct ScaleRows {  // byte offset of each row's scales (rows clamped into the matrix)
+  int64_t w[WBLK_N];
+  int64_t x[WBLK_T];
+};
+
+__device__ __forceinline__ ScaleRows scale_rows(const FwdParams& p, int64_t t0, int n0, int arow0, int brow0) {
+  ScaleRows sr;
+  const int kb = p.K / 32;
+#pragma unroll
+  for (int nb = 0; nb < WBLK_N; ++nb) {
+    int n = n0 + arow0 + 32 * nb;
+    if (n >= p.N) n = p.N - 1;
+    sr.w[nb] = (int64_t)n * kb;
+  }
+#pragma unroll
+  for (int tb = 0; tb < WBLK_T; ++tb) {
+    int64_t t = t0 + brow0 + 32 * tb;
+    if (t >= p.T) t = p.T - 1;
+    sr.x[tb] = t * kb;
+  }
+  return sr;
+}
+
+__device__ __forceinline__ StageScales load_scales(const FwdParams& p, const ScaleRows& sr, int kt, int nk) {
+  const int k4 = 4 * (kt < nk ? kt : nk - 1);
+  StageScales sc;
+#pragma unroll
+  for (int nb = 0; nb < WBLK_N; ++nb) sc.w[nb] = *reinterpret_cast<const uint32_t*>(p.ws + sr.w[nb] + k4);
+#pragma unroll
+  for (int tb = 0; tb < WBLK_T; ++tb) sc.x[tb] = *reinterpret_cast<const uint32_t*>(p.xs + sr.x[tb] + k4);
+  return sc;
+}
+
 template <int MODE>
 __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const uint8_t* cur,
-                                          const uint8_t* xsc, const uint8_t* wsc, int kblocks, int kt,
-                                          int arow0, int brow0, int half) {
+                                          const StageScales& sc, int arow0, int brow0, int half) {
   using TL = Tile<MODE>;
   if (!TL::MX) {
     // all fragments of the stage's k16 steps first, so the later steps' LDS
@@ -404,19 +440,19 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
     // the slice, lane half h reads the whole 16-byte chunk 2 jb + h, whose
     // first and last 8 codes feed two k16 steps.
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      const int kblk = 2 * kt + jb;
+    for (int jb = 0; jb < TL::KPS / 32; ++jb) {
       const int c = 2 * jb + half;
       bf16x8_t a0[WBLK_N], a1[WBLK_N], b0[WBLK_T], b1[WBLK_T];
 #pragma unroll
       for (int nb = 0; nb < WBLK_N; ++nb) {
         const int r = arow0 + 32 * nb;
-        frag_mx_exact(cur + TL::XSB + r * TL::ROWB, c, r, e8m0_to_f32(wsc[kblk * TILE_N + r]), a0[nb], a1[nb]);
+        frag_mx_exact(cur + TL::XSB + r * TL::ROWB, c, r, e8m0_to_f32((sc.w[nb] >> (8 * jb)) & 0xFFu),
+                      a0[nb], a1[nb]);
       }
 #pragma unroll
       for (int tb = 0; tb < WBLK_T; ++tb) {
         const int r = brow0 + 32 * tb;
-        frag_mx_exact(cur + r * TL::ROWB, c, r, e8m0_to_f32(xsc[kblk * TILE_T + r]), b0[tb], b1[tb]);
+        frag_mx_exact(cur + r * TL::ROWB, c, r, e8m0_to_f32((sc.x[tb] >> (8 * jb)) & 0xFFu), b0[tb], b1[tb]);
       }
 #pragma unroll
       for (int nb = 0; nb < WBLK_N; ++nb)
@@ -430,58 +466,42 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
           acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[nb], b1[tb], acc[nb][tb], 0, 0, 0);
     }
   } else {
-    // Scaled FP8 32x32x64: lane (row, half) holds 16 bytes of K-block 0
-    // (k = 16 half .. +15) in its first four registers and 16 bytes of
-    // K-block 1 (k = 32 + 16 half .. +15) in the last four; the E8M0 scale
-    // of (row, block b) is taken from lane row + 32 b, byte 0.
-    const int kblk = 2 * kt + half;
-    i32x8_t a[WBLK_N], b[WBLK_T];
-    uint32_t sa[WBLK_N], sb[WBLK_T];
+    // Scaled FP8 32x32x64, two per 128-value slice (s = 0, 1): lane
+    // (row, half) holds 16 bytes of K-block 2s (k = 64 s + 16 half .. +15) in
+    // its first four registers and 16 bytes of K-block 2s+1 (k = 64 s + 32 +
+    // 16 half .. +15) in the last four; the E8M0 scale of (row, block b) is
+    // taken from lane row + 32 b, byte 0, so each lane passes the scale of
+    // block 2s + half of its row.
 #pragma unroll
-    for (int nb = 0; nb < WBLK_N; ++nb) {
-      const int r = arow0 + 32 * nb;
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + TL::XSB + roff<64>(r, half));
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + TL::XSB + roff<64>(r, 2 + half));
-      a[nb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      sa[nb] = wsc[kblk * TILE_N + r];
+    for (int st = 0; st < TL::KPS / 64; ++st) {
+      i32x8_t a[WBLK_N], b[WBLK_T];
+      uint32_t sa[WBLK_N], sb[WBLK_T];
+      const int sh = 8 * (2 * st + half);
+#pragma unroll
+      for (int nb = 0; nb < WBLK_N; ++nb) {
+        const int r = arow0 + 32 * nb;
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + TL::XSB + roff<128>(r, 4 * st + half));
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + TL::XSB + roff<128>(r, 4 * st + 2 + half));
+        a[nb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        sa[nb] = (sc.w[nb] >> sh) & 0xFFu;
+      }
+#pragma unroll
+      for (int tb = 0; tb < WBLK_T; ++tb) {
+        const int r = brow0 + 32 * tb;
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + roff<128>(r, 4 * st + half));
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + roff<128>(r, 4 * st + 2 + half));
+        b[tb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        sb[tb] = (sc.x[tb] >> sh) & 0xFFu;
+      }
+#pragma unroll
+      for (int nb = 0; nb < WBLK_N; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < WBLK_T; ++tb)
+          acc[nb][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              a[nb], b[tb], acc[nb][tb], 0, 0, 0, (int)sa[nb], 0, (int)sb[tb]);
     }
-#pragma unroll
-    for (int tb = 0; tb < WBLK_T; ++tb) {
-      const int r = brow0 + 32 * tb;
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + roff<64>(r, half));
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + roff<64>(r, 2 + half));
-      b[tb] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      sb[tb] = xsc[kblk * TILE_T + r];
-    }
-#pragma unroll
-    for (int nb = 0; nb < WBLK_N; ++nb)
-#pragma unroll
-      for (int tb = 0; tb < WBLK_T; ++tb)
-        acc[nb][tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            a[nb], b[tb], acc[nb][tb], 0, 0, 0, (int)sa[nb], 0, (int)sb[tb]);
-  }
-}
-
-// MXFP8 operand scales of a tile (all K blocks of its X and W rows) copied
-// into LDS with ordinary loads before the main loop, transposed to
-// [K block][row] so the 32 rows a wave reads are consecutive bytes.
-__device__ __forceinline__ void load_tile_scales(const FwdParams& p, int64_t t0, int n0, uint8_t* xsc,
-                                                 uint8_t* wsc, int tid) {
-  const int kb = p.K / 32;
-  // consecutive threads take consecutive rows: consecutive LDS bytes
-  for (int e = tid; e < TILE_T * kb; e += NTHREADS) {
-    const int c = e / TILE_T, r = e - c * TILE_T;
-    int64_t t = t0 + r;
-    if (t >= p.T) t = p.T - 1;
-    xsc[e] = p.xs[t * kb + c];
-  }
-  for (int e = tid; e < TILE_N * kb; e += NTHREADS) {
-    const int c = e / TILE_N, r = e - c * TILE_N;
-    int n = n0 + r;
-    if (n >= p.N) n = p.N - 1;
-    wsc[e] = p.ws[(int64_t)n * kb + c];
   }
 }
 
@@ -493,9 +513,7 @@ void qup_fwd_kernel(FwdParams p) {
   constexpr int KPS = TL::KPS;
   constexpr int STAGES = TL::STAGES;
   constexpr int RING = TL::SB * STAGES;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING + (MX ? XSC_BYTES + WSC_BYTES : 0)];
-  uint8_t* xsc = lds + RING;
-  uint8_t* wsc = xsc + XSC_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -509,7 +527,6 @@ void qup_fwd_kernel(FwdParams p) {
   const TileGrid g{grid.tiles_t, grid.tiles_n, grid.tiles_t * grid.tiles_n};
   const int row_bytes = MX ? p.K : 2 * p.K;
   const int nk = p.K / KPS;
-  const int kblocks = p.K / 32;
   const uint8_t* xb = static_cast<const uint8_t*>(p.x);
   const uint8_t* wb = static_cast<const uint8_t*>(p.w);
   const uint32_t ring = lds_u32(lds);
@@ -522,12 +539,12 @@ void qup_fwd_kernel(FwdParams p) {
   int64_t t0 = (int64_t)tt * TILE_T;
   int n0 = tn * TILE_N;
   DmaPlan<MODE> dp = dma_plan<MODE>(p, t0, n0, wave, lane, row_bytes);
-  if (MX) {
-    load_tile_scales(p, t0, n0, xsc, wsc, tid);
-    __syncthreads();
-  }
+  ScaleRows sr{};
+  StageScales sc_next{}, sc_cur{};
+  if (MX) sr = scale_rows(p, t0, n0, arow0, brow0);
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, s, ring, wave);
+  if (MX) sc_next = load_scales(p, sr, 0, nk);  // MX: STAGES == 2, one stage ahead
 
   for (;;) {
     f32x16_t acc[WBLK_N][WBLK_T];
@@ -546,7 +563,13 @@ void qup_fwd_kernel(FwdParams p) {
       // (kt + STAGES - 1) % STAGES was read in iteration kt - 1 and every
       // wave has passed the barrier since.
       issue_stage<MODE>(dp, xb, wb, kt + STAGES - 1, nk, kt + STAGES - 1, ring, wave);
-      mma_stage<MODE>(acc, lds + (kt % STAGES) * TL::SB, xsc, wsc, kblocks, kt, arow0, brow0, half);
+      if (MX) {
+        // stage kt's scales arrived with its DMA (the wait above covers all
+        // vector loads); stage kt + 1's go out with its DMA
+        sc_cur = sc_next;
+        sc_next = load_scales(p, sr, kt + 1, nk);
+      }
+      mma_stage<MODE>(acc, lds + (kt % STAGES) * TL::SB, sc_cur, arow0, brow0, half);
     }
 
     // Next tile of this workgroup: start its first stages before the
@@ -564,16 +587,14 @@ void qup_fwd_kernel(FwdParams p) {
       dp = dma_plan<MODE>(p, t0, n0, wave, lane, row_bytes);
 #pragma unroll
       for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, s, ring, wave);
+      if (MX) {
+        sr = scale_rows(p, t0, n0, arow0, brow0);
+        sc_next = load_scales(p, sr, 0, nk);
+      }
     }
     epilogue_tile(p, tm, acc, n0c + 32 * WBLK_N * wn, t0c + 32 * WBLK_T * wt + (lane & 31), lane);
     if (!more) break;
     u = un;
-    if (MX) {
-      // the scale area is only read inside the main loop: every wave passed
-      // the barrier above after its last read
-      load_tile_scales(p, t0, n0, xsc, wsc, tid);
-      __syncthreads();
-    }
   }
 }
 
@@ -587,7 +608,6 @@ int fwd_grid(const FwdParams& p, int num_cus) {
   return (int)(tiles < g ? tiles : g);
 }
 
-bool fwd_scales_fit(int K) { return K / 32 <= MAX_KBLOCKS; }
 
 hipError_t launch_qup_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const dim3 grid(fwd_grid(p, device_cu_count()));

@@ -121,8 +121,9 @@ def test_fwd_validation_mx_and_thd(L):
     mx = dict(x_dtype=bd.DTYPE_MXFP8, w_dtype=bd.DTYPE_MXFP8)
     assert fwd(L, **mx) == bd.MLA_EINVAL                          # scales missing
     assert fwd(L, **mx, x_scales=addr(7), w_scales=addr(8), K=1600) == bd.MLA_EINVAL  # K % 128
-    # the forward keeps a tile's operand scales in LDS: K <= 2048 for MXFP8 operands
-    assert fwd(L, **mx, x_scales=addr(7), w_scales=addr(8), K=2176) == bd.MLA_EUNSUPPORTED
+    # operand scales are read as dwords: 4-byte alignment
+    assert fwd(L, **mx, x_scales=addr(7, 2), w_scales=addr(8)) == bd.MLA_EINVAL
+    assert fwd(L, **mx, x_scales=addr(7), w_scales=addr(8, 1)) == bd.MLA_EINVAL
     thd = dict(tokens__fmt=bd.FMT_THD, tokens__cu_seqlens=addr(9), tokens__nseq=2,
                tokens__max_seqlen=200)
     assert fwd(L, **{**thd, "tokens__nseq": 0}) == bd.MLA_EINVAL

@@ -204,16 +204,16 @@ def test_fwd_mxfp8_projection_small():
     full_compare_fwd(x, w, H=H, dn=128, dr=64, B=1, S=T, mx_in=True)
 
 
-def test_fwd_mxfp8_projection_largest_k():
-    """K = 2048, the largest K whose operand scales fit the forward tile's LDS
-    scale area (64 blocks per row); ragged token tile."""
-    T, K, H = 96, 2048, 2
+def test_fwd_mxfp8_projection_long_k():
+    """K = 4096 (operand scales stream with each stage, so K has no limit
+    beyond the 32-bit row offsets); ragged token tile."""
+    T, K, H = 96, 4096, 2
     x = syn.normal_bf16((T, K), 1.0, 44)
     w = syn.normal_bf16((H * 192, K), 0.02, 45)
     full_compare_fwd(x, w, H=H, dn=128, dr=64, B=1, S=T, mx_in=True)
 
 
-@pytest.mark.parametrize("fp8_mfma,K", [(False, 512), (True, 512), (False, 2048), (True, 2048)])
+@pytest.mark.parametrize("fp8_mfma,K", [(False, 512), (True, 512), (False, 2176), (True, 2176)])
 def test_fwd_mxfp8_operands_narrow_codes_random_scales(fp8_mfma, K):
     """MXFP8 X and W given directly: every code has exponent field 7 (values
     +-1..1.875), scales vary per 32-block. Products then never differ by more
@@ -237,8 +237,12 @@ def test_fwd_mxfp8_operands_narrow_codes_random_scales(fp8_mfma, K):
                                     pos=pos, x_scales=xs, w_scales=ws)
     g = o.bf16_bits_to_f64(bits16(out[0].transpose(0, 1)))
     r = o.bf16_bits_to_f64(o.f32_to_bf16_bits(q64.astype(np.float32)))
-    # bf16 rounding of values that agree to fp32 accuracy: at most one bf16 step apart
-    assert (np.abs(g - r) <= np.abs(r) * 2.0 ** -7 + 1e-30).all()
+    # g and r are bf16 roundings (half a step, 2^-8 relative, each) of values
+    # within the fp32 accumulation bound of the exact result
+    lim = 2.0 ** -7 * np.abs(q64) + 1.01 * bound + 1e-30
+    ratio = np.abs(g - r) / lim
+    print(f"\nnarrow codes K={K} fp8_mfma={fp8_mfma}: worst |g-r| / bound = {ratio.max():.3g}")
+    assert (ratio <= 1).all()
 
 
 def test_fwd_fp8_mfma_mode_accuracy():
