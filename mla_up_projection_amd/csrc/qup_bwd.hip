@@ -159,10 +159,10 @@ __global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict_
 // Persistent, two independent 256-thread workgroups per CU, tile 192 (i) x
 // 128 (j); waves 2 x 2, each 96 (i) x 64 (j) = 3 x 2 blocks of the 32x32x16
 // MFMA (P is the MFMA's row operand, so a lane holds 4 consecutive i of one j:
-// 16-byte fp32 or 8-byte bf16 stores). The reduction streams through a 4-slot
-// LDS ring of 32-value stages filled by direct global->LDS DMA in memory
-// order; nothing is transposed on the way in.
-//   * MN-major stage = 32 rows (r) x tile width, row pitch RP = 2 x width.
+// 16-byte stores). The reduction streams through an LDS ring (2 slots of
+// 64-value stages, or 4 slots of 32-value stages) filled by direct
+// global->LDS DMA in memory order; nothing is transposed on the way in.
+//   * MN-major stage = KS rows (r) x tile width, row pitch RP = 2 x width.
 //     Fragments come from ds_read_b64_tr_b16: within each 16-lane group, lane
 //     i receives element i%4 of the 8-byte row slices addressed by lanes
 //     4e + i/4 (e = 0..3). Lane 16g+s addresses row 8(g/2) + 4h + s/4 (h = 0,
@@ -173,8 +173,9 @@ __global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict_
 //     64-byte segments are XOR-swizzled per row so those 4 land in distinct
 //     bank quarters: segment s ^ (r & 3) when RP is a multiple of 256 bytes,
 //     s ^ ((r >> 1) & 1) when RP = 128 mod 256.
-//   * K-major stage = tile rows x 64 bytes, 16-byte chunk c of row r stored at
-//     c ^ ((r >> 2) & 3), read with ds_read_b128 as in the forward.
+//   * K-major stage = tile rows x 2 KS bytes, 16-byte chunk c of row r stored
+//     at c ^ ((r >> 2) & 3) (64-byte rows) or c ^ ((r >> 1) & 7) (128-byte
+//     rows), read with ds_read_b128 as in the forward.
 //   * A reduction tail (r past the end inside the last stage) is read from a
 //     clamped row and zeroed in both MN-major fragments before the MFMA. A
 //     K-major Q requires a reduction length that is a multiple of 32.

@@ -19,13 +19,13 @@
 //     runs of 4 consecutive head-dim elements of one token: RoPE pairs are
 //     lane-local and a 32-element scale block is split between lanes l and
 //     l^32 (one xor-shuffle for its amax).
-//   * K streams through an LDS ring (4 slots for bf16, 3 for E4M3) of 64-byte
-//     row slices (32 bf16 or 64 E4M3 K-values per row per stage), filled by
-//     direct global->LDS DMA (global_load_lds_dwordx4) issued STAGES-1
-//     stages ahead; each wave counts
-//     its own outstanding DMA with s_waitcnt vmcnt and one s_barrier per
-//     stage publishes the slot. The main loop issues no other vector-memory
-//     instruction, so the counts are exact.
+//   * K streams through an LDS ring of row slices (128 bytes per row and
+//     stage in 2 slots; 64 bytes in 4 slots for bf16 with K % 64 == 32),
+//     filled by direct global->LDS DMA (global_load_lds_dwordx4) issued
+//     STAGES-1 stages ahead; each wave counts its own outstanding loads with
+//     s_waitcnt vmcnt and one s_barrier per stage publishes the slot. The
+//     only other vector-memory loads in the loop are the MXFP8 operand
+//     scales, issued with the stage they belong to.
 //   * After the last stage of a tile, the first stages of the workgroup's
 //     next tile are put in flight before the epilogue runs.
 //   * Tiles are ordered so that the 64 workgroups resident on one XCD share
