@@ -225,6 +225,15 @@ def main():
     parts["qup_fwd_thd_yarn_16384"] = {"ms": ms4, "tflops": tf4, "pct_bf16_peak": 100 * tf4 / BF16_PEAK_TFLOPS,
                                        "sequences": len(w4.lengths)}
     del x4, out4
+    # context: the vendor library GEMM (torch -> hipBLASLt) on the same three
+    # products, bf16 out, with no epilogue and no inverse RoPE
+    dq2 = dq.reshape(T, N)
+    lib = {}
+    for name, fn in (("fwd_x_wT", lambda: torch.nn.functional.linear(x, w)),
+                     ("dx_dq_w", lambda: torch.mm(dq2, w)),
+                     ("dw_dqT_x", lambda: torch.mm(dq2.t(), x))):
+        lib[name + "_ms"] = timed(fn, R)
+    parts["context_library_gemm_bf16"] = lib
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device=dev)
