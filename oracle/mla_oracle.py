@@ -401,3 +401,62 @@ def qup_backward(dq, x, w, *, H, d_nope, d_rope, cos, sin, fmt=FMT_BSHD, B=1, S=
     dq_pre = rope_rotate(dqf.reshape(T, H, d_nope + d_rope), pos, cos, sin,
                          d_nope, d_rope, inverse=True).reshape(T, -1)
     return BwdResult(dq_pre, dq_pre @ wf, dq_pre.T @ xf, dq_pre.sum(axis=0))
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 backward -- the "mxfp8 projection" of [FWD, description] carried into
+# the linear backward that [BWD, Greptile summary] routes the pre-RoPE
+# gradient through. The pages name no further detail; the reading taken is
+# the MXFP8 training recipe of the library the pages extend: every operand of
+# a product is quantized along that product's reduction axis [OCP-MX], from
+# the stored bf16 dq_pre and the bf16 x and W:
+#   dX = deq(Q_rows(dq_pre)) . deq(Q_cols(W))     (reduction over n)
+#   dW = deq(Q_cols(dq_pre))^T . deq(Q_cols(x))   (reduction over tokens)
+#   db = sum over tokens of dq_pre (unquantized, as in the bf16 backward).
+# Q_rows blocks 32 consecutive elements of a row, Q_cols 32 consecutive rows
+# of a column; the token axis is zero-padded to a multiple of 32.
+# ---------------------------------------------------------------------------
+def mxfp8_quantize_columns(v: np.ndarray):
+    """MXFP8-quantize along the first axis: blocks of 32 consecutive rows of
+    each column [OCP-MX], rows zero-padded to a multiple of 32. The result is
+    returned transposed, the blocked axis contiguous: codes uint8 [C, Rp] and
+    scales uint8 [C, Rp/32]."""
+    v32 = np.asarray(v, dtype=np.float32)
+    R, C = v32.shape
+    Rp = -(-R // 32) * 32
+    vp = np.zeros((Rp, C), dtype=np.float32)
+    vp[:R] = v32
+    return mxfp8_quantize_blocks(np.ascontiguousarray(vp.T))
+
+
+@dataclass
+class MxBwdResult:
+    dq_pre: np.ndarray       # float64 [T, N], before the bf16 store
+    dq_pre_bf16: np.ndarray  # uint16 [T, N], the stored copy the operands come from
+    dx: np.ndarray           # float64 [T, K]
+    dw: np.ndarray           # float64 [N, K]
+    db: np.ndarray           # float64 [N]
+    dq_rows: tuple           # (codes [T, N], scales [T, N/32])
+    dq_cols_t: tuple         # (codes [N, Tp], scales [N, Tp/32])
+    w_cols_t: tuple          # (codes [K, N], scales [K, N/32])
+    x_cols_t: tuple          # (codes [K, Tp], scales [K, Tp/32])
+
+
+def qup_backward_mxfp8(dq, x, w, *, H, d_nope, d_rope, cos, sin, fmt=FMT_BSHD, B=1, S=None,
+                       cu_seqlens=None) -> MxBwdResult:
+    """The backward with MXFP8 operands (see the section comment above).
+
+    dq_pre is the inverse RoPE of dq, stored as bf16 (rounded once to float32,
+    the kernel's precision, then to bf16); both products read that copy.
+    """
+    r = qup_backward(dq, x, w, H=H, d_nope=d_nope, d_rope=d_rope, cos=cos, sin=sin, fmt=fmt,
+                     B=B, S=S, cu_seqlens=cu_seqlens)
+    bits = f32_to_bf16_bits(r.dq_pre.astype(np.float32))
+    dqp = bf16_bits_to_f64(bits)
+    rows = mxfp8_quantize_blocks(dqp)
+    dq_t = mxfp8_quantize_columns(dqp)
+    w_t = mxfp8_quantize_columns(to_f64(w))
+    x_t = mxfp8_quantize_columns(to_f64(x))
+    dx = mxfp8_dequantize(*rows) @ mxfp8_dequantize(*w_t).T
+    dw = mxfp8_dequantize(*dq_t) @ mxfp8_dequantize(*x_t).T
+    return MxBwdResult(r.dq_pre, bits, dx, dw, r.db, rows, dq_t, w_t, x_t)

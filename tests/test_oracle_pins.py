@@ -451,3 +451,136 @@ def test_oracle_leaves_inputs_untouched():
     o.qup_forward(xt, Wt, H=w.H, d_nope=w.d_nope, d_rope=w.d_rope, cos=cos, sin=sin, B=1, S=w.T)
     assert torch.equal(xt.view(torch.int16), x0.view(torch.int16))
     assert torch.equal(Wt.view(torch.int16), W0.view(torch.int16))
+
+
+# ------------------------------------------------------ MXFP8 backward ----
+def test_mx_columns_hand_worked():
+    # [OCP-MX] worked by hand: 33 rows (padded to 64), two columns.
+    # column 0 = [2^20, 1 x 31, 3]: block 0 amax 2^20 -> E = 20 - 8 = 12, 2^20 -> 256 = code 0x78,
+    # 1 * 2^-12 is below half the smallest E4M3 subnormal (2^-9) -> 0; block 1 = [3, 0 x 31]
+    # -> E = 1 - 8 = -7, 3 * 2^7 = 384 = 1.5 * 2^8 -> code 0x7C. Column 1 = ones: E = -8,
+    # 1 -> 256 = 0x78; its second block holds one 1 and padding zeros.
+    v = np.ones((33, 2))
+    v[0, 0] = 2.0 ** 20
+    v[32, 0] = 3.0
+    codes, scales = o.mxfp8_quantize_columns(v)
+    assert codes.shape == (2, 64) and scales.shape == (2, 2)
+    assert codes[0, 0] == 0x78 and not codes[0, 1:32].any()
+    assert codes[0, 32] == 0x7C and not codes[0, 33:].any()
+    assert (codes[1, :33] == 0x78).all() and not codes[1, 33:].any()
+    assert scales.tolist() == [[12 + 127, -7 + 127], [-8 + 127, -8 + 127]]
+
+
+def _mx_bwd(dq, x, w, H, dn, dr, T, seed=0):
+    cos, sin = o.rope_table(T, max(dr, 2), 10000.0) if dr else (np.ones((T, 1)), np.zeros((T, 1)))
+    return o.qup_backward_mxfp8(torch.from_numpy(dq.astype(np.float32)).to(torch.bfloat16),
+                                torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16),
+                                torch.from_numpy(w.astype(np.float32)).to(torch.bfloat16),
+                                H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin)
+
+
+def test_mx_backward_exact_when_representable():
+    # Every block's amax in [4, 7] gives E = -6, and k * 64 (|k| <= 7) is an E4M3 value:
+    # quantization is lossless, so the products equal the plain ones. T = 40 exercises the
+    # zero-padded token blocks.
+    rng = np.random.default_rng(5)
+    T, H, D, K = 40, 2, 32, 64
+    pick = lambda *s: rng.choice([-7, -6, -5, -4, 4, 5, 6, 7], size=s).astype(np.float64)
+    dq, x, w = pick(T, H * D), pick(T, K), pick(H * D, K)
+    r = _mx_bwd(dq.reshape(T, H, D), x, w, H, D, 0, T)
+    assert np.array_equal(r.dx, dq @ w)
+    assert np.array_equal(r.dw, dq.T @ x)
+    assert np.array_equal(r.db, dq.sum(axis=0))
+
+
+def test_mx_backward_orientation_hand_worked():
+    # dq (32 x 32, one head without rope): dq[0,0] = 2^20, the rest of row 0 is 1, the
+    # rest of column 0 is 2, everything else 1. Row quantization (dX operand) flushes the
+    # ones of token 0 (1 * 2^-12 -> 0) and keeps every other row exactly; column
+    # quantization (dW operand) flushes the twos of column 0 (2 * 2^-12 -> 0) and keeps
+    # every other column. W = 2 I and x = 3 I then expose each quantized operand.
+    T = N = K = 32
+    dq = np.ones((T, N))
+    dq[1:, 0] = 2.0
+    dq[0, 0] = 2.0 ** 20
+    w = 2.0 * np.eye(N, K)
+    x = 3.0 * np.eye(T, K)
+    r = _mx_bwd(dq.reshape(T, 1, N), x, w, 1, N, 0, T)
+    ex = 2.0 * dq
+    ex[0, 1:] = 0.0
+    ew = 3.0 * dq.T
+    ew[0, 1:] = 0.0
+    assert np.array_equal(r.dx, ex)
+    assert np.array_equal(r.dw, ew)
+
+
+def test_mx_backward_power_of_two_scaling():
+    # Scaling by a power of two moves every block exponent and nothing else.
+    rng = np.random.default_rng(6)
+    T, H, dn, dr, K = 48, 2, 32, 32, 64
+    D = dn + dr
+    dq = rng.standard_normal((T, H, D))
+    x = rng.standard_normal((T, K))
+    w = rng.standard_normal((H * D, K))
+    a = _mx_bwd(dq, x, w, H, dn, dr, T)
+    b = _mx_bwd(dq * 8.0, x, w, H, dn, dr, T)
+    c = _mx_bwd(dq, x * 0.25, w, H, dn, dr, T)
+    assert np.array_equal(b.dx, 8.0 * a.dx) and np.array_equal(b.dw, 8.0 * a.dw)
+    assert np.array_equal(c.dw, 0.25 * a.dw) and np.array_equal(c.dx, a.dx)
+
+
+def test_mx_backward_within_quantization_bound():
+    # Each quantized operand element is within 2^-4 of its value relative (E4M3, 3 mantissa
+    # bits, round to nearest) plus 2^(E-10) absolute (half the subnormal step of its block);
+    # the products' error is bounded by the sum of those terms. Also a gross check that
+    # the MXFP8 products track the unquantized ones.
+    rng = np.random.default_rng(7)
+    T, H, dn, dr, K = 64, 2, 32, 32, 96
+    D = dn + dr
+    dq = rng.standard_normal((T, H, D))
+    x = rng.standard_normal((T, K))
+    w = rng.standard_normal((H * D, K)) * 0.05
+    r = _mx_bwd(dq, x, w, H, dn, dr, T)
+    a = o.bf16_bits_to_f64(r.dq_pre_bf16)
+    xf = o.to_f64(torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16))
+    wf = o.to_f64(torch.from_numpy(w.astype(np.float32)).to(torch.bfloat16))
+
+    def err(v, scales_along_rows):  # per-element bound, scales broadcast over their block
+        s = o.e8m0_decode(scales_along_rows)
+        return 2.0 ** -4 * np.abs(v) + np.repeat(s, 32, axis=-1)[..., :v.shape[-1]] * 2.0 ** -10
+    ea = err(a, r.dq_rows[1])
+    ew = err(wf.T, r.w_cols_t[1]).T
+    bound_dx = ea @ np.abs(wf) + np.abs(a) @ ew + ea @ ew
+    assert (np.abs(r.dx - a @ wf) <= bound_dx * (1 + 1e-12)).all()
+    eat = err(a.T, r.dq_cols_t[1][:, :T // 32 + (T % 32 > 0)])
+    ex = err(xf.T, r.x_cols_t[1]).T
+    bound_dw = eat @ np.abs(xf) + np.abs(a.T) @ ex + eat @ ex
+    assert (np.abs(r.dw - a.T @ xf) <= bound_dw * (1 + 1e-12)).all()
+    rel = np.linalg.norm(r.dx - a @ wf) / np.linalg.norm(a @ wf)
+    assert 1e-4 < rel < 0.05
+
+
+def test_mx_backward_quantizes_the_stored_bf16_copy():
+    # The operands are quantized from dq_pre as stored (bf16), not from its exact value.
+    # Pick g_a, g_b so that v = c g_a + s g_b (inverse rotation at position 1, pair 0)
+    # lies in (1.0625, 1.0625 + 2^-9): bf16 rounds v down to 1.0625 exactly. The block
+    # amax is in [1, 2), so E = -8 and the E4M3 grid near 1.0625 * 256 = 272 has step 32:
+    # 272 is a tie between 256 (code 0x78) and 288 (0x79), broken to even -> 0x78; the
+    # unrounded v would round up to 0x79.
+    T, H, dn, dr, K = 2, 1, 32, 32, 32
+    cos, sin = o.rope_table(T, dr, 10000.0)
+    c, s = float(np.float32(cos[1, 0])), float(np.float32(sin[1, 0]))
+    grid = o.bf16_bits_to_f64(np.arange(0x3F00, 0x3FC0, dtype=np.uint16))  # 0.5 .. 1.5
+    va = grid[:, None] * c + grid[None, :] * s
+    i, j = np.argwhere((va > 1.0625) & (va < 1.0625 + 2.0 ** -9))[0]
+    ga, gb = grid[i], grid[j]
+    assert abs(-ga * s + gb * c) < 2.0
+    dq = np.zeros((T, H, dn + dr))
+    dq[1, 0, dn] = ga
+    dq[1, 0, dn + 1] = gb
+    x = np.ones((T, K))
+    w = np.ones((H * (dn + dr), K))
+    r = _mx_bwd(dq, x, w, H, dn, dr, T)
+    assert o.bf16_bits_to_f64(r.dq_pre_bf16[1:2, dn:dn + 1])[0, 0] == 1.0625
+    assert r.dq_rows[1][1, dn // 32] == 127 - 8
+    assert r.dq_rows[0][1, dn] == 0x78
