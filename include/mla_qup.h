@@ -139,6 +139,26 @@ MLA_API mla_status rope_cache_build(float* cos, float* sin, int32_t rows, int32_
 MLA_API mla_status mxfp8_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
                           int64_t ld, uint8_t* codes, uint8_t* scales, void* stream);
 
+/* MXFP8-quantize a row-major bf16 matrix along its COLUMNS (blocks of 32
+ * consecutive rows of a column) and store the result transposed, the blocked
+ * axis contiguous: the operand layout of a product that reduces over the
+ * matrix's rows. Used by mla_qup_bwd_mxfp8 for W, x and dq_pre (the forward
+ * page's mxfp8 projection carried into the backward page's linear backward;
+ * each operand is quantized along its product's reduction axis). Same block
+ * rule as mxfp8_quantize; rows r in [rows, rows_pad) count as zeros.
+ *   x       : device bf16, element (r, c) at x[r*ld + c]; 16-byte aligned,
+ *             ld a multiple of 8.
+ *   rows >= 0; cols > 0, a multiple of 8, at most 4194240; ld >= cols;
+ *   rows_pad >= rows, a multiple of 32.
+ *   codes_t : device uint8[cols*rows_pad], element (c, r) at
+ *             codes_t[c*rows_pad + r]; 16-byte aligned.
+ *   scales_t: device uint8[cols*rows_pad/32], block (c, r/32) at
+ *             scales_t[c*(rows_pad/32) + r/32].
+ * Errors: MLA_EINVAL, MLA_EALIAS. */
+MLA_API mla_status mxfp8_quantize_t(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                                    int64_t rows_pad, uint8_t* codes_t, uint8_t* scales_t,
+                                    void* stream);
+
 /* Forward: Q = X W^T (+ bias), RoPE on pairs (2i, 2i+1) of each head's rope
  * slice (head layout [nope | rope], D = d_nope + d_rope, N = H*D), written
  * out of place in BHSD, as BF16 or MXFP8 (one E8M0 scale per 32 elements
@@ -212,6 +232,25 @@ MLA_API size_t mla_qup_bwd_workspace_size(const mla_qup_bwd_args* args);
 /* Errors: MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EWORKSPACE,
  * MLA_EDEVICE. */
 MLA_API mla_status mla_qup_bwd(const mla_qup_bwd_args* args, void* stream);
+
+/* MXFP8 backward: the forward page's "mxfp8 projection" carried into the
+ * backward page's linear backward. Same arguments, outputs and dq_pre / db
+ * as mla_qup_bwd; the two products take MXFP8 operands, each quantized
+ * along its product's reduction axis (OCP MX: blocks of 32, E8M0 scale,
+ * E4M3 round-to-nearest-even, saturating) from the stored bf16 dq_pre and
+ * the bf16 x and W:
+ *   dx = deq(Q_along_n(dq_pre)) . deq(Q_along_n(W))        (reduction over n)
+ *   dw = deq(Q_along_t(dq_pre))^T . deq(Q_along_t(x))      (reduction over t)
+ * The token axis is zero-padded for the blocks along t. Accumulation fp32.
+ *   fp8_mfma: 0 = products on exact bf16 MFMA of the dequantized operands,
+ *             1 = the scaled FP8 MFMA (its internal precision is lower).
+ * Extra shape limits: N = H*D a multiple of 128, K a multiple of 32, and
+ * T*N, N*ceil128(T), K*N, K*ceil128(T) each below 2^32 (else MLA_EUNSUPPORTED).
+ * Workspace: mla_qup_bwd_mxfp8_workspace_size() bytes (quantized operands
+ * and dX split partials), 256-B aligned.
+ * Errors: as mla_qup_bwd, plus MLA_EUNSUPPORTED. */
+MLA_API size_t mla_qup_bwd_mxfp8_workspace_size(const mla_qup_bwd_args* args);
+MLA_API mla_status mla_qup_bwd_mxfp8(const mla_qup_bwd_args* args, int32_t fp8_mfma, void* stream);
 
 /* Static string naming a status code. */
 MLA_API const char* mla_status_str(mla_status status);

@@ -21,8 +21,9 @@ MLA_OK, MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EUNSUPPORTED, MLA_EDEVICE, 
 DTYPE_BF16, DTYPE_FP32, DTYPE_MXFP8 = 0, 1, 2
 FMT_BSHD, FMT_SBHD, FMT_THD = 0, 1, 2
 
-FUNCTIONS = ("rope_cache_build", "mxfp8_quantize", "mla_qup_fwd", "mla_qup_bwd",
-             "mla_qup_bwd_workspace_size", "mla_status_str")
+FUNCTIONS = ("rope_cache_build", "mxfp8_quantize", "mxfp8_quantize_t", "mla_qup_fwd", "mla_qup_bwd",
+             "mla_qup_bwd_workspace_size", "mla_qup_bwd_mxfp8", "mla_qup_bwd_mxfp8_workspace_size",
+             "mla_status_str")
 
 
 class mla_tokens(Structure):
@@ -72,13 +73,19 @@ def lib() -> ctypes.CDLL:
                                        POINTER(mla_yarn), c_void_p]
         L.mxfp8_quantize.argtypes = [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p,
                                      c_void_p, c_void_p]
+        L.mxfp8_quantize_t.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_int64, c_void_p,
+                                       c_void_p, c_void_p]
         L.mla_qup_fwd.argtypes = [POINTER(mla_qup_fwd_args), c_void_p]
         L.mla_qup_bwd.argtypes = [POINTER(mla_qup_bwd_args), c_void_p]
         L.mla_qup_bwd_workspace_size.argtypes = [POINTER(mla_qup_bwd_args)]
         L.mla_qup_bwd_workspace_size.restype = c_size_t
+        L.mla_qup_bwd_mxfp8.argtypes = [POINTER(mla_qup_bwd_args), c_int32, c_void_p]
+        L.mla_qup_bwd_mxfp8_workspace_size.argtypes = [POINTER(mla_qup_bwd_args)]
+        L.mla_qup_bwd_mxfp8_workspace_size.restype = c_size_t
         L.mla_status_str.argtypes = [c_int32]
         L.mla_status_str.restype = c_char_p
-        for f in ("rope_cache_build", "mxfp8_quantize", "mla_qup_fwd", "mla_qup_bwd"):
+        for f in ("rope_cache_build", "mxfp8_quantize", "mxfp8_quantize_t", "mla_qup_fwd", "mla_qup_bwd",
+                  "mla_qup_bwd_mxfp8"):
             getattr(L, f).restype = c_int32
         _lib = L
     return _lib
@@ -166,6 +173,20 @@ def mxfp8_quantize(x, codes, scales, stream=None):
     _check(st, "mxfp8_quantize")
 
 
+def mxfp8_quantize_t(x, codes_t, scales_t, rows_pad=None, stream=None):
+    """x bf16 [rows, cols] (row stride may exceed cols) -> codes_t uint8
+    [cols, rows_pad], scales_t uint8 [cols, rows_pad/32]: quantized along the
+    columns, stored transposed; rows_pad defaults to codes_t.shape[1]."""
+    if x.stride(-1) != 1:
+        raise ValueError("x rows must be contiguous")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    rp = codes_t.shape[1] if rows_pad is None else rows_pad
+    st = lib().mxfp8_quantize_t(x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), rp,
+                                _ptr(codes_t), _ptr(scales_t), _stream(stream))
+    _check(st, "mxfp8_quantize_t")
+
+
 def make_fwd_args(x, w, out, *, H, d_nope, d_rope, cos=None, sin=None, x_scales=None,
                   w_scales=None, bias=None, out_scales=None, fmt=FMT_BSHD, B=1, S=None,
                   cu_seqlens=None, max_seqlen=None, fp8_mfma=False) -> mla_qup_fwd_args:
@@ -223,3 +244,19 @@ def mla_qup_bwd(dq, x, w, dq_pre, *, stream=None, **kw):
     mla_qup_bwd_workspace_size() bytes (None if that is 0)."""
     a = make_bwd_args(dq, x, w, dq_pre, **kw)
     _check(lib().mla_qup_bwd(ctypes.byref(a), _stream(stream)), "mla_qup_bwd")
+
+
+def mla_qup_bwd_mxfp8_workspace_size(dq, x, w, dq_pre, **kw) -> int:
+    kw.pop("stream", None)
+    kw.pop("fp8_mfma", None)
+    a = make_bwd_args(dq, x, w, dq_pre, **kw)
+    return int(lib().mla_qup_bwd_mxfp8_workspace_size(ctypes.byref(a)))
+
+
+def mla_qup_bwd_mxfp8(dq, x, w, dq_pre, *, fp8_mfma=False, stream=None, **kw):
+    """MXFP8 backward: arguments and outputs as mla_qup_bwd; the dx and dw
+    products take MXFP8 operands quantized along their reduction axes.
+    workspace: at least mla_qup_bwd_mxfp8_workspace_size() bytes."""
+    a = make_bwd_args(dq, x, w, dq_pre, **kw)
+    _check(lib().mla_qup_bwd_mxfp8(ctypes.byref(a), 1 if fp8_mfma else 0, _stream(stream)),
+           "mla_qup_bwd_mxfp8")

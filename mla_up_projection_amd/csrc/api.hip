@@ -165,6 +165,22 @@ mla_status mxfp8_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t 
                                              scales, (hipStream_t)stream));
 }
 
+mla_status mxfp8_quantize_t(const void* x, int64_t rows, int64_t cols, int64_t ld, int64_t rows_pad,
+                            uint8_t* codes_t, uint8_t* scales_t, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 8 != 0 || cols > 65535LL * 64 || ld < cols || ld % 8 != 0)
+    return MLA_EINVAL;
+  if (rows_pad < rows || rows_pad % 32 != 0 || rows_pad > ((int64_t)1 << 40)) return MLA_EINVAL;
+  if (rows_pad == 0) return MLA_OK;
+  if (x == nullptr || codes_t == nullptr || scales_t == nullptr) return MLA_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes_t, 16)) return MLA_EINVAL;
+  const size_t xbytes = rows ? ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * 2 : 0;
+  if (overlaps({rng(codes_t, (size_t)cols * rows_pad), rng(scales_t, (size_t)cols * rows_pad / 32)},
+               {rng(x, xbytes)}))
+    return MLA_EALIAS;
+  return launched(mla::launch_mxfp8_quantize_t(x, rows, cols, ld, rows_pad, codes_t, scales_t,
+                                               (hipStream_t)stream));
+}
+
 mla_status mla_qup_fwd(const mla_qup_fwd_args* a, void* stream) {
   if (a == nullptr) return MLA_EINVAL;
   mla_status st = check_head_shape(a->K, a->H, a->d_nope, a->d_rope);
@@ -256,7 +272,31 @@ size_t mla_qup_bwd_workspace_size(const mla_qup_bwd_args* a) {
   return mla::plan_bwd(a->tokens.T, N, a->K, a->use_bias != 0, a->dx != nullptr).total;
 }
 
-mla_status mla_qup_bwd(const mla_qup_bwd_args* a, void* stream) {
+static bool mx_bwd_shapes_ok(int64_t T, int N, int K) {
+  const int64_t Tp = (T + 127) / 128 * 128;
+  const int64_t lim = (int64_t)1 << 32;
+  return N % 128 == 0 && K % 32 == 0 && T * N < lim && (int64_t)N * Tp < lim && (int64_t)K * N < lim &&
+         (int64_t)K * Tp < lim;
+}
+
+size_t mla_qup_bwd_mxfp8_workspace_size(const mla_qup_bwd_args* a) {
+  int64_t max_pos = 0;
+  if (check_bwd_shapes(a, &max_pos) != MLA_OK) return 0;
+  const int N = a->H * (a->d_nope + a->d_rope);
+  if (!mx_bwd_shapes_ok(a->tokens.T, N, a->K)) return 0;
+  return mla::plan_bwd_mx(a->tokens.T, N, a->K, a->use_bias != 0).total;
+}
+
+static mla_status qup_bwd_impl(const mla_qup_bwd_args* a, int mx, int fp8_mfma, void* stream);
+
+mla_status mla_qup_bwd(const mla_qup_bwd_args* a, void* stream) { return qup_bwd_impl(a, 0, 0, stream); }
+
+mla_status mla_qup_bwd_mxfp8(const mla_qup_bwd_args* a, int32_t fp8_mfma, void* stream) {
+  if (fp8_mfma != 0 && fp8_mfma != 1) return MLA_EINVAL;
+  return qup_bwd_impl(a, 1, fp8_mfma, stream);
+}
+
+static mla_status qup_bwd_impl(const mla_qup_bwd_args* a, int mx, int fp8_mfma, void* stream) {
   int64_t max_pos = 0;
   mla_status st = check_bwd_shapes(a, &max_pos);
   if (st) return st;
@@ -271,7 +311,14 @@ mla_status mla_qup_bwd(const mla_qup_bwd_args* a, void* stream) {
       !aligned(a->dq_pre, 16) || (a->dx && !aligned(a->dx, 16)) || (a->dw && !aligned(a->dw, 16)) ||
       (a->db && !aligned(a->db, 2)))
     return MLA_EINVAL;
+  if (mx && !mx_bwd_shapes_ok(T, N, a->K)) return MLA_EUNSUPPORTED;
   mla::BwdPlan plan = mla::plan_bwd(T, N, a->K, a->use_bias != 0, a->dx != nullptr);
+  mla::MxBwdPlan mplan{};
+  if (mx) {
+    mplan = mla::plan_bwd_mx(T, N, a->K, a->use_bias != 0);
+    plan = mplan.base;
+    plan.total = mplan.total;
+  }
   if (plan.total > 0) {
     if (a->workspace == nullptr || a->workspace_bytes < plan.total) return MLA_EWORKSPACE;
     if (!aligned(a->workspace, 256)) return MLA_EINVAL;
@@ -314,6 +361,7 @@ mla_status mla_qup_bwd(const mla_qup_bwd_args* a, void* stream) {
   p.use_bias = a->use_bias;
   p.db = (uint16_t*)a->db;
   p.workspace = a->workspace;
+  if (mx) return launched(mla::launch_qup_bwd_mx(p, mplan, fp8_mfma, (hipStream_t)stream));
   return launched(mla::launch_qup_bwd(p, plan, (hipStream_t)stream));
 }
 

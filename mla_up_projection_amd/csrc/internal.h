@@ -25,6 +25,11 @@ struct FwdParams {
   int rope_rows, rope_pairs;
   int out_mx;              // 1: MXFP8 codes + scales, 0: bf16
   int mx_fp8_mfma;         // MXFP8 operands on the scaled FP8 MFMA (else exact bf16 MFMA)
+  // plain product form (launch_mx_gemm): out[t][n] row-major with stride N,
+  // fp32 when out_f32 (else bf16); K split into k_splits stage ranges, range
+  // s writing at out + s * split_stride bytes
+  int out_f32, k_splits;
+  int64_t split_stride;
   void* out;
   uint8_t* out_scales;
 };
@@ -58,6 +63,19 @@ struct BwdPlan {
   size_t dx_off, dx_bytes;
   size_t total;
 };
+// MXFP8 backward workspace: the bf16 backward's db partials, then the
+// quantized operands (offsets in bytes, 256-aligned) and dX split partials.
+struct MxBwdPlan {
+  BwdPlan base;
+  int64_t Tp;                    // tokens padded to a multiple of 128
+  size_t dq_rows, dq_rows_sc;    // dq_pre along n: codes [T, N], scales [T, N/32]
+  size_t dq_t, dq_t_sc;          // dq_pre along t, transposed: [N, Tp], [N, Tp/32]
+  size_t w_t, w_t_sc;            // W along n, transposed: [K, N], [K, N/32]
+  size_t x_t, x_t_sc;            // X along t, transposed: [K, Tp], [K, Tp/32]
+  int dx_splits;                 // reduction splits of dX (fp32 partials [splits, T, K])
+  size_t dx_part;
+  size_t total;
+};
 BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx);
 
 // Compute units of the current device (cached per device; 0 if unknown).
@@ -65,11 +83,20 @@ int device_cu_count();
 
 hipError_t launch_rope_cache(float* cos, float* sin, int rows, int d_rope, double base,
                              const mla_yarn* yarn, hipStream_t stream);
+hipError_t launch_mxfp8_quantize_t(const void* x, int64_t rows, int64_t cols, int64_t ld, int64_t rows_pad,
+                                   uint8_t* codes_t, uint8_t* scales_t, hipStream_t stream);
 hipError_t launch_mxfp8_quantize(const void* x, int x_fp32, int64_t rows, int64_t cols,
                                  int64_t ld, uint8_t* codes, uint8_t* scales,
                                  hipStream_t stream);
 hipError_t launch_qup_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_qup_fwd_mx(const FwdParams& p, hipStream_t stream);
+// MXFP8 x MXFP8 product out[t][n] = sum_k X[t][k] W[n][k] in the plain form
+// (FwdParams: x, xs, w, ws, T, K, N, mx_fp8_mfma, out, out_f32, k_splits,
+// split_stride; K % 128 == 0).
+hipError_t launch_mx_gemm(const FwdParams& p, hipStream_t stream);
+int mx_gemm_tiles(int64_t rows, int cols);
 hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& plan, hipStream_t stream);
+MxBwdPlan plan_bwd_mx(int64_t T, int N, int K, bool use_bias);
+hipError_t launch_qup_bwd_mx(const BwdParams& p, const MxBwdPlan& pl, int fp8_mfma, hipStream_t stream);
 
 }  // namespace mla

@@ -16,6 +16,9 @@
 //                     reduction axis is strided in memory is transposed by the
 //                     LDS transpose read (ds_read_b64_tr_b16).
 //   split_reduce_kernel: ordered sum of the dX reduction splits -> bf16.
+//   launch_qup_bwd_mx: the MXFP8 backward (operands quantized along each
+//                     product's reduction axis, products on the forward
+//                     kernel's MXFP8 main loop).
 // No floating-point atomics anywhere: results are run-to-run deterministic.
 #include <algorithm>
 
@@ -704,6 +707,130 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
       hipLaunchKernelGGL((bgemm_kernel<false, 64, false>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 backward: each product's operands quantized along its reduction axis
+// (the forward page's mxfp8 projection carried into the backward page's
+// linear backward), then the forward kernel's MXFP8 main loop in its plain
+// product form:
+//   dX[t][k] = sum_n Qrow(dq_pre)[t][n] Qcol(W)[n][k]  ("tokens" t, "rows" k)
+//   dW[n][k] = sum_t Qcol(dq_pre)[t][n] Qcol(X)[t][k]  ("tokens" n, "rows" k)
+// Column-quantized operands are stored transposed (reduction axis
+// contiguous), so both products read two K-major operands; the token axis is
+// zero-padded to a multiple of 128 (one MXFP8 stage).
+// ---------------------------------------------------------------------------
+static int mx_split_count(int64_t tiles, int64_t stages) {
+  const int cus = device_cu_count();
+  const int64_t slots = (int64_t)(cus > 0 ? cus : 256) * 2;
+  int best = 1;
+  int64_t best_cost = ((tiles + slots - 1) / slots) * stages;
+  for (int s = 2; s <= 8; ++s) {
+    const int64_t sps = (stages + s - 1) / s;
+    if (sps < 4) break;
+    const int64_t cost = ((tiles * s + slots - 1) / slots) * sps;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  // the kernel gives each split ceil(stages / splits) stages: no split may
+  // start past the end
+  int s = best;
+  while (s > 1 && (int64_t)(s - 1) * ((stages + s - 1) / s) >= stages) --s;
+  return s;
+}
+
+MxBwdPlan plan_bwd_mx(int64_t T, int N, int K, bool use_bias) {
+  MxBwdPlan pl{};
+  pl.base = plan_bwd(T, N, K, use_bias, false);
+  pl.Tp = (T + 127) / 128 * 128;
+  size_t off = pl.base.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  pl.dq_rows = take((size_t)T * N);
+  pl.dq_rows_sc = take((size_t)T * N / 32);
+  pl.dq_t = take((size_t)N * pl.Tp);
+  pl.dq_t_sc = take((size_t)N * pl.Tp / 32);
+  pl.w_t = take((size_t)K * N);
+  pl.w_t_sc = take((size_t)K * N / 32);
+  pl.x_t = take((size_t)K * pl.Tp);
+  pl.x_t_sc = take((size_t)K * pl.Tp / 32);
+  pl.dx_splits = T > 0 ? mx_split_count(mx_gemm_tiles(T, K), N / 128) : 1;
+  pl.dx_part = pl.dx_splits > 1 ? take((size_t)pl.dx_splits * T * K * 4) : 0;
+  pl.total = T > 0 ? off : 0;
+  return pl;
+}
+
+hipError_t launch_qup_bwd_mx(const BwdParams& p, const MxBwdPlan& pl, int fp8_mfma, hipStream_t stream) {
+  if (p.T == 0) return launch_qup_bwd(p, pl.base, stream);  // zero dW and db
+  uint8_t* ws = static_cast<uint8_t*>(p.workspace);
+  // dq_pre and db exactly as the bf16 backward (no dX / dW products there)
+  BwdParams q = p;
+  q.dx = nullptr;
+  q.dw = nullptr;
+  hipError_t e = launch_qup_bwd(q, pl.base, stream);
+  if (e != hipSuccess) return e;
+  const int64_t T = p.T;
+  const int N = p.N, K = p.K;
+  if (p.dx) {
+    if ((e = launch_mxfp8_quantize(p.dq_pre, 0, T, N, N, ws + pl.dq_rows, ws + pl.dq_rows_sc, stream)))
+      return e;
+    if ((e = launch_mxfp8_quantize_t(p.w, N, K, K, N, ws + pl.w_t, ws + pl.w_t_sc, stream))) return e;
+    FwdParams g{};
+    g.x = ws + pl.dq_rows;
+    g.xs = ws + pl.dq_rows_sc;
+    g.w = ws + pl.w_t;
+    g.ws = ws + pl.w_t_sc;
+    g.T = T;
+    g.K = N;
+    g.N = K;
+    g.H = 1;
+    g.D = K;
+    g.d_nope = K;
+    g.B = 1;
+    g.S = (int)T;
+    g.mx_fp8_mfma = fp8_mfma;
+    g.k_splits = pl.dx_splits;
+    const bool split = pl.dx_splits > 1;
+    g.out_f32 = split;
+    g.split_stride = (int64_t)T * K * 4;
+    g.out = split ? static_cast<void*>(ws + pl.dx_part) : static_cast<void*>(p.dx);
+    if ((e = launch_mx_gemm(g, stream))) return e;
+    if (split) {
+      const int64_t n4 = T * K / 4;
+      hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                         reinterpret_cast<const float*>(ws + pl.dx_part), pl.dx_splits, n4, p.dx);
+      if ((e = hipGetLastError())) return e;
+    }
+  }
+  if (p.dw) {
+    if ((e = launch_mxfp8_quantize_t(p.dq_pre, T, N, N, pl.Tp, ws + pl.dq_t, ws + pl.dq_t_sc, stream)))
+      return e;
+    if ((e = launch_mxfp8_quantize_t(p.x, T, K, K, pl.Tp, ws + pl.x_t, ws + pl.x_t_sc, stream))) return e;
+    FwdParams g{};
+    g.x = ws + pl.dq_t;
+    g.xs = ws + pl.dq_t_sc;
+    g.w = ws + pl.x_t;
+    g.ws = ws + pl.x_t_sc;
+    g.T = N;
+    g.K = (int)pl.Tp;
+    g.N = K;
+    g.H = 1;
+    g.D = K;
+    g.d_nope = K;
+    g.B = 1;
+    g.S = N;
+    g.mx_fp8_mfma = fp8_mfma;
+    g.k_splits = 1;
+    g.out_f32 = p.dw_fp32;
+    g.out = p.dw;
+    if ((e = launch_mx_gemm(g, stream))) return e;
   }
   return hipSuccess;
 }

@@ -49,6 +49,7 @@ static_assert(WBLK_N == 3, "packed scale stores below are written for 3 blocks p
 constexpr int WG_PER_CU = 2;              // two independent workgroups per CU
 
 enum { MODE_BF16 = 0, MODE_MX_EXACT = 1, MODE_MX_FP8 = 2, MODE_BF16_R64 = 3 };
+enum { EPI_MLA = 0, EPI_PLAIN = 1 };  // fused RoPE/quantize/BHSD epilogue, or a plain row-major store
 
 // Stage layout per mode: a ring slot holds ROWB bytes of each of the tile's
 // TILE_T X rows and TILE_N W rows. 128-byte row slices (whole cache lines per
@@ -280,9 +281,9 @@ struct TileGrid {
 // Tile u -> (token tile, n tile). Workgroup g runs on XCD g % 8 and takes
 // tiles g, g + G, g + 2G, ... (G a multiple of 8), so every tile of one XCD
 // has u % 8 == xcd; v = xcd * (total / 8) + u / 8 gives each XCD a contiguous
-// run of v. v is then decoded in groups of 4 token tiles: 32 consecutive v
-// (one round of the XCD's 32 resident workgroups) cover 4 token tiles x 8 n
-// tiles, whose K slices the XCD's L2 serves to all 32 at once.
+// run of v. v is then decoded in groups of 8 token tiles: 64 consecutive v
+// (one round of the XCD's 64 resident workgroups) cover 8 token tiles x 8 n
+// tiles, whose K slices the XCD's L2 serves to all 64 at once.
 constexpr int GROUP_T = 8;
 __device__ __forceinline__ void tile_coords(const TileGrid& g, int u, int& tt, int& tn) {
   int v = u;
@@ -379,20 +380,22 @@ struct ScaleRows {  // byte offset of each row's scales (rows clamped into the m
   int64_t x[WBLK_T];
 };
 
-__device__ __forceinline__ ScaleRows scale_rows(const FwdParams& p, int64_t t0, int n0, int arow0, int brow0) {
+__device__ __forceinline__ ScaleRows scale_rows(const FwdParams& p, int64_t t0, int n0, int arow0, int brow0,
+                                                int kt0) {
   ScaleRows sr;
   const int kb = p.K / 32;
+  const int64_t k4 = 4 * (int64_t)kt0;  // 4 scale bytes per 128-value stage
 #pragma unroll
   for (int nb = 0; nb < WBLK_N; ++nb) {
     int n = n0 + arow0 + 32 * nb;
     if (n >= p.N) n = p.N - 1;
-    sr.w[nb] = (int64_t)n * kb;
+    sr.w[nb] = (int64_t)n * kb + k4;
   }
 #pragma unroll
   for (int tb = 0; tb < WBLK_T; ++tb) {
     int64_t t = t0 + brow0 + 32 * tb;
     if (t >= p.T) t = p.T - 1;
-    sr.x[tb] = t * kb;
+    sr.x[tb] = t * kb + k4;
   }
   return sr;
 }
@@ -505,7 +508,86 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
   }
 }
 
-template <int MODE>
+// Plain row-major store of one 32 x 32 block, out[t][n] with row stride N,
+// bf16 or fp32 (no bias, no rotation): the product form the MXFP8 backward
+// uses. Lanes l and l^32 trade 4-row groups so that each lane owns 16
+// consecutive n (lower lane rows 0..15, upper 16..31).
+__device__ __forceinline__ void plain_block(const FwdParams& p, uint8_t* out, int64_t t, bool ok,
+                                            const f32x16_t& acc, int n_blk, int lane) {
+  const int half = lane >> 5;
+  if (p.out_f32) {
+    u32x2_t r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      // by value: a bit cast of a vector element lvalue reads element 0 here
+      r[j] = swap_halves(__float_as_uint(acc[j]), __float_as_uint(acc[8 + j]));
+    if (ok) {
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (t * p.N + n_blk + 16 * half) * 4);
+      dst[0] = u32x4_t{r[0][0], r[1][0], r[2][0], r[3][0]};
+      dst[1] = u32x4_t{r[0][1], r[1][1], r[2][1], r[3][1]};
+      dst[2] = u32x4_t{r[4][0], r[5][0], r[6][0], r[7][0]};
+      dst[3] = u32x4_t{r[4][1], r[5][1], r[6][1], r[7][1]};
+    }
+  } else {
+    uint32_t P[8];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      P[2 * g] = pack_bf16x2(acc[4 * g + 0], acc[4 * g + 1]);
+      P[2 * g + 1] = pack_bf16x2(acc[4 * g + 2], acc[4 * g + 3]);
+    }
+    u32x2_t r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = swap_halves(P[k], P[4 + k]);
+    if (ok) {
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (t * p.N + n_blk + 16 * half) * 2);
+      dst[0] = u32x4_t{r[0][0], r[1][0], r[0][1], r[1][1]};
+      dst[1] = u32x4_t{r[2][0], r[3][0], r[2][1], r[3][1]};
+    }
+  }
+}
+
+__device__ __forceinline__ void plain_tile(const FwdParams& p, uint8_t* out,
+                                           const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int64_t t_lane,
+                                           int lane) {
+#pragma unroll
+  for (int tb = 0; tb < WBLK_T; ++tb) {
+    const int64_t t = t_lane + 32 * tb;
+#pragma unroll
+    for (int nb = 0; nb < WBLK_N; ++nb) {
+      const int n_blk = n0 + 32 * nb;
+      if (n_blk < p.N) plain_block(p, out, t, t < p.T, acc[nb][tb], n_blk, lane);
+    }
+  }
+}
+
+// Work unit u -> tile and K range. The fused forward runs every tile over
+// the whole K; the plain product form may split K into p.k_splits ranges of
+// equal stage counts (unit u: range u / tiles, tile u % tiles), each range
+// writing its own fp32 partial output.
+struct Unit {
+  int tt, tn;   // token tile, n tile
+  int kt0, nk;  // first stage and stage count
+  int split;
+};
+template <int EPI>
+__device__ __forceinline__ Unit unit_coords(const TileGrid& g, const FwdParams& p, int u, int nk_all) {
+  Unit w;
+  if (EPI == EPI_PLAIN) {
+    w.split = u / g.total;
+    const int per = (nk_all + p.k_splits - 1) / p.k_splits;
+    w.kt0 = w.split * per;
+    w.nk = min(per, nk_all - w.kt0);
+    tile_coords(g, u - w.split * g.total, w.tt, w.tn);
+  } else {
+    w.split = 0;
+    w.kt0 = 0;
+    w.nk = nk_all;
+    tile_coords(g, u, w.tt, w.tn);
+  }
+  return w;
+}
+
+template <int MODE, int EPI>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(WG_PER_CU, WG_PER_CU)))
 void qup_fwd_kernel(FwdParams p) {
   using TL = Tile<MODE>;
@@ -526,22 +608,24 @@ void qup_fwd_kernel(FwdParams p) {
   const TileGrid grid{(int)((p.T + TILE_T - 1) / TILE_T), (p.N + TILE_N - 1) / TILE_N, 0};
   const TileGrid g{grid.tiles_t, grid.tiles_n, grid.tiles_t * grid.tiles_n};
   const int row_bytes = MX ? p.K : 2 * p.K;
-  const int nk = p.K / KPS;
-  const uint8_t* xb = static_cast<const uint8_t*>(p.x);
-  const uint8_t* wb = static_cast<const uint8_t*>(p.w);
+  const int nk_all = p.K / KPS;
+  const int units = EPI == EPI_PLAIN ? g.total * p.k_splits : g.total;
   const uint32_t ring = lds_u32(lds);
   const TokenMap tm{p.fmt, p.B, p.S, p.cu, p.nseq};
 
   int u = blockIdx.x;
-  if (u >= g.total) return;
-  int tt, tn;
-  tile_coords(g, u, tt, tn);
-  int64_t t0 = (int64_t)tt * TILE_T;
-  int n0 = tn * TILE_N;
+  if (u >= units) return;
+  Unit un_ = unit_coords<EPI>(g, p, u, nk_all);
+  int64_t t0 = (int64_t)un_.tt * TILE_T;
+  int n0 = un_.tn * TILE_N;
+  int nk = un_.nk;
+  // operand bases at the unit's first stage (stage indices below are relative)
+  const uint8_t* xb = static_cast<const uint8_t*>(p.x) + (int64_t)un_.kt0 * TL::ROWB;
+  const uint8_t* wb = static_cast<const uint8_t*>(p.w) + (int64_t)un_.kt0 * TL::ROWB;
   DmaPlan<MODE> dp = dma_plan<MODE>(p, t0, n0, wave, lane, row_bytes);
   ScaleRows sr{};
   StageScales sc_next{}, sc_cur{};
-  if (MX) sr = scale_rows(p, t0, n0, arow0, brow0);
+  if (MX) sr = scale_rows(p, t0, n0, arow0, brow0, un_.kt0);
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, s, ring, wave);
   if (MX) sc_next = load_scales(p, sr, 0, nk);  // MX: STAGES == 2, one stage ahead
@@ -575,24 +659,32 @@ void qup_fwd_kernel(FwdParams p) {
     // Next tile of this workgroup: start its first stages before the
     // epilogue of the current one.
     const int un = u + gridDim.x;
-    const bool more = un < g.total;
+    const bool more = un < units;
     const int64_t t0c = t0;
     const int n0c = n0;
+    const int split_c = un_.split;
     vm_wait<0>();
     barrier();
     if (more) {
-      tile_coords(g, un, tt, tn);
-      t0 = (int64_t)tt * TILE_T;
-      n0 = tn * TILE_N;
+      un_ = unit_coords<EPI>(g, p, un, nk_all);
+      t0 = (int64_t)un_.tt * TILE_T;
+      n0 = un_.tn * TILE_N;
+      nk = un_.nk;
+      xb = static_cast<const uint8_t*>(p.x) + (int64_t)un_.kt0 * TL::ROWB;
+      wb = static_cast<const uint8_t*>(p.w) + (int64_t)un_.kt0 * TL::ROWB;
       dp = dma_plan<MODE>(p, t0, n0, wave, lane, row_bytes);
 #pragma unroll
       for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, s, ring, wave);
       if (MX) {
-        sr = scale_rows(p, t0, n0, arow0, brow0);
+        sr = scale_rows(p, t0, n0, arow0, brow0, un_.kt0);
         sc_next = load_scales(p, sr, 0, nk);
       }
     }
-    epilogue_tile(p, tm, acc, n0c + 32 * WBLK_N * wn, t0c + 32 * WBLK_T * wt + (lane & 31), lane);
+    if (EPI == EPI_PLAIN)
+      plain_tile(p, static_cast<uint8_t*>(p.out) + (int64_t)split_c * p.split_stride, acc,
+                 n0c + 32 * WBLK_N * wn, t0c + 32 * WBLK_T * wt + (lane & 31), lane);
+    else
+      epilogue_tile(p, tm, acc, n0c + 32 * WBLK_N * wn, t0c + 32 * WBLK_T * wt + (lane & 31), lane);
     if (!more) break;
     u = un;
   }
@@ -612,18 +704,35 @@ int fwd_grid(const FwdParams& p, int num_cus) {
 hipError_t launch_qup_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const dim3 grid(fwd_grid(p, device_cu_count()));
   if (p.K % 64 == 0)
-    hipLaunchKernelGGL(qup_fwd_kernel<MODE_BF16>, grid, dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((qup_fwd_kernel<MODE_BF16, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
   else
-    hipLaunchKernelGGL(qup_fwd_kernel<MODE_BF16_R64>, grid, dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((qup_fwd_kernel<MODE_BF16_R64, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_qup_fwd_mx(const FwdParams& p, hipStream_t stream) {
   const dim3 grid(fwd_grid(p, device_cu_count()));
   if (p.mx_fp8_mfma)
-    hipLaunchKernelGGL(qup_fwd_kernel<MODE_MX_FP8>, grid, dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_FP8, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
   else
-    hipLaunchKernelGGL(qup_fwd_kernel<MODE_MX_EXACT>, grid, dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_EXACT, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+int mx_gemm_tiles(int64_t rows, int cols) {
+  return (int)(((rows + TILE_T - 1) / TILE_T) * ((cols + TILE_N - 1) / TILE_N));
+}
+
+hipError_t launch_mx_gemm(const FwdParams& p, hipStream_t stream) {
+  const int64_t units = (int64_t)mx_gemm_tiles(p.T, p.N) * p.k_splits;
+  int64_t g = (int64_t)device_cu_count() * WG_PER_CU;
+  if (g % 8) g -= g % 8;
+  if (g < 8) g = 8;
+  const dim3 grid((unsigned)(units < g ? units : g));
+  if (p.mx_fp8_mfma)
+    hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_FP8, EPI_PLAIN>), grid, dim3(NTHREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_EXACT, EPI_PLAIN>), grid, dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 

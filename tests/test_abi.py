@@ -180,6 +180,36 @@ def test_bwd_validation(L, over, code):
     assert L.mla_qup_bwd(ctypes.byref(bwd_args(**over)), None) == code
 
 
+def test_bwd_mxfp8_workspace_and_validation(L):
+    # T = 256, N = 4 * 192 = 768, K = 1536: db partials, then the quantized operands,
+    # each 256-byte aligned (all of these sizes already are); dX needs no split here
+    # (16 tiles, 6 stages of 128).
+    T, N, K = 256, 768, 1536
+    expect = (4 * N * 4) + T * N + T * N // 32 + N * T + N * T // 32 + K * N + K * N // 32 \
+        + K * T + K * T // 32
+    assert L.mla_qup_bwd_mxfp8_workspace_size(ctypes.byref(bwd_args())) == expect
+    assert L.mla_qup_bwd_mxfp8_workspace_size(ctypes.byref(bwd_args(use_bias=0))) == expect - 4 * N * 4
+    # N = 3 * 192 = 576 is not a multiple of 128
+    assert L.mla_qup_bwd_mxfp8_workspace_size(ctypes.byref(bwd_args(H=3))) == 0
+    assert L.mla_qup_bwd_mxfp8(ctypes.byref(bwd_args(H=3)), 0, None) == bd.MLA_EUNSUPPORTED
+    assert L.mla_qup_bwd_mxfp8(ctypes.byref(bwd_args()), 2, None) == bd.MLA_EINVAL
+    small = L.mla_qup_bwd_workspace_size(ctypes.byref(bwd_args()))
+    assert L.mla_qup_bwd_mxfp8(ctypes.byref(bwd_args(workspace_bytes=small)), 0, None) == bd.MLA_EWORKSPACE
+    assert L.mla_qup_bwd_mxfp8(ctypes.byref(bwd_args(db=addr(10, 4096))), 1, None) == bd.MLA_EALIAS
+
+
+def test_quantize_t_validation(L):
+    q = L.mxfp8_quantize_t
+    assert q(addr(1), 40, 60, 64, 64, addr(2), addr(3), None) == bd.MLA_EINVAL    # cols % 8
+    assert q(addr(1), 40, 64, 60, 64, addr(2), addr(3), None) == bd.MLA_EINVAL    # ld < cols
+    assert q(addr(1), 40, 64, 68, 64, addr(2), addr(3), None) == bd.MLA_EINVAL    # ld % 8
+    assert q(addr(1), 40, 64, 64, 48, addr(2), addr(3), None) == bd.MLA_EINVAL    # rows_pad % 32
+    assert q(addr(1), 40, 64, 64, 32, addr(2), addr(3), None) == bd.MLA_EINVAL    # rows_pad < rows
+    assert q(addr(1, 8), 40, 64, 64, 64, addr(2), addr(3), None) == bd.MLA_EINVAL  # x alignment
+    assert q(addr(1), 40, 64, 64, 64, addr(1, 256), addr(3), None) == bd.MLA_EALIAS
+    assert q(addr(1), 0, 64, 64, 0, 0, 0, None) == bd.MLA_OK
+
+
 def test_rope_and_quantize_validation(L):
     y = bd.mla_yarn(40.0, 4096, 32.0, 1.0, 1.0)
     assert L.rope_cache_build(None, addr(2), 16, 64, 1e4, None, None) == bd.MLA_EINVAL

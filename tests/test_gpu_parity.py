@@ -309,7 +309,8 @@ def test_fwd_position_beyond_table_is_nan_not_a_read():
 
 # ------------------------------------------------------------ backward ------
 def run_bwd(dq, x, w, *, H, dn, dr, fmt=m.FMT_BSHD, B=1, S=None, cu=None, max_seqlen=None,
-            use_bias=True, dw_fp32=False, yarn=None):
+            use_bias=True, dw_fp32=False, yarn=None, mx=None, want=("dx", "dw")):
+    """mx: None for the bf16 backward, else the fp8_mfma flag of the MXFP8 one."""
     T, K = x.shape
     N = H * (dn + dr)
     S = S if S is not None else T // B
@@ -317,15 +318,21 @@ def run_bwd(dq, x, w, *, H, dn, dr, fmt=m.FMT_BSHD, B=1, S=None, cu=None, max_se
     cos, sin, oc, os_ = rope_tables(max_pos, dr, yarn=yarn)
     dqd, xd, wd = _dev(dq), _dev(x), _dev(w)
     dq_pre = torch.empty(T, N, dtype=torch.bfloat16, device=DEV)
-    dx = torch.empty(T, K, dtype=torch.bfloat16, device=DEV)
-    dw = torch.empty(N, K, dtype=torch.float32 if dw_fp32 else torch.bfloat16, device=DEV)
+    dx = torch.empty(T, K, dtype=torch.bfloat16, device=DEV) if "dx" in want else None
+    dw = torch.empty(N, K, dtype=torch.float32 if dw_fp32 else torch.bfloat16, device=DEV) \
+        if "dw" in want else None
     db = torch.empty(N, dtype=torch.bfloat16, device=DEV) if use_bias else None
     kw = dict(H=H, d_nope=dn, d_rope=dr, cos=cos if dr else None, sin=sin if dr else None,
               dx=dx, dw=dw, db=db, use_bias=use_bias, fmt=fmt, B=B, S=S,
               cu_seqlens=_dev(cu) if cu is not None else None, max_seqlen=max_seqlen)
-    nbytes = m.mla_qup_bwd_workspace_size(dqd, xd, wd, dq_pre, **kw)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
-    m.mla_qup_bwd(dqd, xd, wd, dq_pre, workspace=ws if nbytes else None, **kw)
+    if mx is None:
+        nbytes = m.mla_qup_bwd_workspace_size(dqd, xd, wd, dq_pre, **kw)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+        m.mla_qup_bwd(dqd, xd, wd, dq_pre, workspace=ws if nbytes else None, **kw)
+    else:
+        nbytes = m.mla_qup_bwd_mxfp8_workspace_size(dqd, xd, wd, dq_pre, **kw)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+        m.mla_qup_bwd_mxfp8(dqd, xd, wd, dq_pre, fp8_mfma=mx, workspace=ws if nbytes else None, **kw)
     torch.cuda.synchronize()
     return dict(dq_pre=dq_pre, dx=dx, dw=dw, db=db, oc=oc, os=os_)
 
@@ -434,6 +441,95 @@ def test_bwd_zero_tokens_zeroes_dw_db():
     assert (dw.float() == 0).all() and (db.float() == 0).all()
 
 
+# ------------------------------------------------------- MXFP8 backward ----
+def test_mxfp8_quantize_t_bitexact():
+    """Column quantization with a transposed store: 200 rows padded to 224
+    (a partial 128-row tile), special values, bit for bit against the oracle."""
+    R, C, Rp = 200, 96, 224
+    x = syn.normal_bf16((R, C), 1.0, 150).clone()
+    x[0:32, 3] = 0.0                            # an all-zero block
+    x[40, 5] = float("nan")                     # a NaN block
+    x[70, 6] = float("inf")                     # an infinite block
+    x[100, 7] = 3.0e38                          # saturates its block's other codes to 0
+    x[130:162, 8] = 2.0 ** -130                 # subnormal-range block
+    codes = torch.full((C, Rp), 0xAA, dtype=torch.uint8, device=DEV)
+    scales = torch.full((C, Rp // 32), 0xAA, dtype=torch.uint8, device=DEV)
+    m.mxfp8_quantize_t(_dev(x), codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = o.mxfp8_quantize_columns(o.to_f64(x))
+    assert rc.shape == (C, Rp)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
+def _check_mx_bwd(g, r, what, fp8_mfma=False):
+    """The dequantized operand products are exact in float32, so the only
+    error against the oracle is float32 accumulation (far below 1e-6 here),
+    the output rounding (bf16: at most 2^-9 relative per element, so a
+    relative Frobenius error below 2^-9), the scaled FP8 MFMA's lower internal
+    precision in that mode (bounded at 1e-3), and the rare operand code that
+    differs because dq_pre's bf16 store rounded a float32 value the oracle
+    holds in float64 (one E4M3 step on one element)."""
+    check_bf16(bits16(g["dq_pre"]), r.dq_pre_bf16, f"{what} dq_pre")
+    out = {}
+    for k in ("dx", "dw"):
+        if g[k] is not None:
+            out[k] = frob_rel(o.to_f64(g[k].cpu()), getattr(r, k))
+            if g[k].dtype == torch.float32:
+                lim = 1e-3 if fp8_mfma else 1e-6
+            else:
+                lim = 2.0 ** -9 * 1.1 + (1e-3 if fp8_mfma else 0.0)
+            assert out[k] <= lim, (what, k, out[k], lim)
+    if g["db"] is not None:
+        assert frob_rel(o.to_f64(g["db"].cpu()), r.db) <= 1e-2
+    print(f"\n{what}: rel Frobenius {out}", flush=True)
+
+
+@pytest.mark.parametrize("fp8_mfma", [False, True])
+def test_bwd_mxfp8_small_against_oracle(fp8_mfma):
+    """T = 333 (tokens padded to 384 for the blocks along t), N = 384, K = 256."""
+    T, K, H = 333, 256, 2
+    x = syn.normal_bf16((T, K), 1.0, 160)
+    w = syn.normal_bf16((H * 192, K), 0.02, 161)
+    dq = syn.normal_bf16((T, H, 192), 1e-3, 162)
+    for dw_fp32 in (False, True):
+        g = run_bwd(dq, x, w, H=H, dn=128, dr=64, S=T, dw_fp32=dw_fp32, mx=fp8_mfma)
+        r = o.qup_backward_mxfp8(dq, x, w, H=H, d_nope=128, d_rope=64, cos=g["oc"], sin=g["os"], S=T)
+        _check_mx_bwd(g, r, f"mx bwd fp8_mfma={fp8_mfma} dw_fp32={dw_fp32}", fp8_mfma)
+
+
+def test_bwd_mxfp8_thd_dx_only_then_dw_only():
+    lengths = [64, 129, 7]
+    cu = syn.cu_seqlens_of(lengths)
+    T, K, H = sum(lengths), 96, 2
+    x = syn.normal_bf16((T, K), 1.0, 170)
+    w = syn.normal_bf16((H * 64, K), 0.05, 171)
+    dq = syn.normal_bf16((T, H, 64), 1e-2, 172)
+    yarn = (40.0, 4096, 32.0, 1.0, 1.0)
+    for want in (("dx",), ("dw",)):
+        g = run_bwd(dq, x, w, H=H, dn=32, dr=32, fmt=m.FMT_THD, cu=cu, max_seqlen=129,
+                    use_bias=False, yarn=yarn, mx=False, want=want, dw_fp32=True)
+        r = o.qup_backward_mxfp8(dq, x, w, H=H, d_nope=32, d_rope=32, cos=g["oc"], sin=g["os"],
+                                 fmt=o.FMT_THD, cu_seqlens=cu.numpy())
+        _check_mx_bwd(g, r, f"mx bwd thd {want}")
+
+
+def test_bwd_mxfp8_zero_tokens_zeroes_dw_db():
+    K, H = 64, 2
+    x = torch.empty(0, K, dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(128, K, dtype=torch.bfloat16, device=DEV)
+    dq = torch.empty(0, H, 64, dtype=torch.bfloat16, device=DEV)
+    dq_pre = torch.empty(0, 128, dtype=torch.bfloat16, device=DEV)
+    dw = torch.full((128, K), 7.0, dtype=torch.bfloat16, device=DEV)
+    db = torch.full((128,), 7.0, dtype=torch.bfloat16, device=DEV)
+    cos = torch.ones(4, 16, device=DEV)
+    cu = torch.zeros(2, dtype=torch.int32, device=DEV)
+    m.mla_qup_bwd_mxfp8(dq, x, w, dq_pre, H=H, d_nope=32, d_rope=32, cos=cos, sin=cos, dw=dw, db=db,
+                        use_bias=True, fmt=m.FMT_THD, cu_seqlens=cu, max_seqlen=1)
+    torch.cuda.synchronize()
+    assert (dw.float() == 0).all() and (db.float() == 0).all()
+
+
 # ------------------------------------------------ full-size named workloads --
 SAMPLE = 96
 
@@ -526,3 +622,36 @@ def test_bwd_full_size_sampled():
     dw_ref = dq_pre[:, nrows].T @ xf
     assert frob_rel(o.to_f64(g["dw"][torch.from_numpy(nrows).to(DEV)].cpu()), dw_ref) <= 1e-2
     assert frob_rel(o.to_f64(g["db"].cpu()), dq_pre.sum(0)) <= 1e-2
+
+
+def test_bwd_mxfp8_full_size_sampled():
+    """DeepSeek-V3 backward with MXFP8 operands, both MFMA modes; sampled dX
+    rows and dW rows against the oracle's steps (the row and column
+    quantizers and the dequantized products)."""
+    wl = syn.workload("dsv3_bwd")
+    x, w, dq = wl.x(), wl.w(), wl.dq()
+    T, K, N = wl.T, wl.K, wl.N
+    pos, _, _ = o.token_coords(o.FMT_BSHD, T, 1, T)
+    rows, nrows = sample_rows(T), sample_rows(N, seed=7)
+    ref = None
+    for fp8 in (False, True):
+        g = run_bwd(dq, x, w, H=wl.H, dn=wl.d_nope, dr=wl.d_rope, S=wl.S, use_bias=True, mx=fp8)
+        if ref is None:
+            dq_pre = o.rope_rotate(o.to_f64(dq), pos, g["oc"], g["os"], wl.d_nope, wl.d_rope,
+                                   inverse=True).reshape(T, N)
+            dqp = o.bf16_bits_to_f64(o.f32_to_bf16_bits(dq_pre.astype(np.float32)))
+            wq = o.mxfp8_dequantize(*o.mxfp8_quantize_columns(o.to_f64(w)))      # [K, N]
+            xq = o.mxfp8_dequantize(*o.mxfp8_quantize_columns(o.to_f64(x)))      # [K, Tp]
+            dx_ref = o.mxfp8_dequantize(*o.mxfp8_quantize_blocks(dqp[rows])) @ wq.T
+            dqc = o.mxfp8_dequantize(*o.mxfp8_quantize_columns(dqp[:, nrows]))   # [n, Tp]
+            dw_ref = dqc @ xq.T
+            ref = (dx_ref, dw_ref, dq_pre.sum(0))
+            del dq_pre, dqp, wq, xq, dqc
+        ri = torch.from_numpy(rows).to(DEV)
+        ni = torch.from_numpy(nrows).to(DEV)
+        ex = frob_rel(o.to_f64(g["dx"][ri].cpu()), ref[0])
+        ew = frob_rel(o.to_f64(g["dw"][ni].cpu()), ref[1])
+        print(f"\nmx bwd dsv3 fp8_mfma={fp8}: dx {ex:.2e} dw {ew:.2e}", flush=True)
+        lim = 2.0 ** -9 * 1.1 + (1e-3 if fp8 else 0.0)
+        assert ex <= lim and ew <= lim
+        assert frob_rel(o.to_f64(g["db"].cpu()), ref[2]) <= 1e-2
