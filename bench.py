@@ -209,6 +209,17 @@ def main():
             "ms": ms2, "tflops": tf, "pct_bf16_peak": 100 * tf / BF16_PEAK_TFLOPS,
             "pct_fp8_peak": 100 * tf / FP8_PEAK_TFLOPS}
     del x2, xq, wq, out2
+    # MXFP8 backward at the same shape: operands quantized along each product's
+    # reduction axis (quantization passes included), both MFMA modes
+    mws_bytes = m.mla_qup_bwd_mxfp8_workspace_size(dq, x, w, dq_pre, **bkw)
+    mws = torch.empty(mws_bytes, dtype=torch.uint8, device=dev)
+    for mode, fp8 in (("exact_bf16_mfma", False), ("fp8_mfma", True)):
+        msb = timed(lambda: m.mla_qup_bwd_mxfp8(dq, x, w, dq_pre, workspace=mws, fp8_mfma=fp8, **bkw), R)
+        tfb = flops_bwd / (msb * 1e-3) / 1e12
+        parts[f"qup_bwd_mxfp8_dsv3_{mode}"] = {"ms": msb, "tflops": tfb,
+                                              "pct_bf16_peak": 100 * tfb / BF16_PEAK_TFLOPS,
+                                              "pct_fp8_peak": 100 * tfb / FP8_PEAK_TFLOPS}
+    del mws
     # packed variable-length (THD) YaRN forward, 16384 tokens, BF16 weight, MXFP8 out
     w4 = syn.workload("thd_yarn_fwd")
     x4 = w4.x().to(dev)
