@@ -460,3 +460,51 @@ def qup_backward_mxfp8(dq, x, w, *, H, d_nope, d_rope, cos, sin, fmt=FMT_BSHD, B
     dx = mxfp8_dequantize(*rows) @ mxfp8_dequantize(*w_t).T
     dw = mxfp8_dequantize(*dq_t) @ mxfp8_dequantize(*x_t).T
     return MxBwdResult(r.dq_pre, bits, dx, dw, r.db, rows, dq_t, w_t, x_t)
+
+
+# ---------------------------------------------------------------------------
+# KV side -- [FWD, flowchart]: the key and the value each go through MXFP8
+# quantization and the same BHSD scale layout as the query before the fused
+# attention; [YQ, Solution]: the KV rotary kernel writes fresh key and value
+# outputs (nothing in place). The pages do not spell out the KV rotary
+# itself; the reading taken is the MLA one the [YQ] page works on: per
+# token, the up-projected kv row holds per head [k_nope | v], and one rope
+# slice k_pe per token, shared by every head, is rotated with the query's
+# table and placed after each head's k_nope:
+#   key[t, h]   = [k_nope[t, h] | rope(k_pe[t], pos_t)]
+#   value[t, h] = v[t, h]
+# The rotated values are float32 (from bf16 inputs) and quantized without
+# an intermediate 16-bit rounding, like the query.
+# ---------------------------------------------------------------------------
+@dataclass
+class KvResult:
+    key32: np.ndarray            # float32 [T, H, d_nope + d_rope], token-major
+    value32: np.ndarray          # float32 [T, H, d_v]
+    key: np.ndarray              # BHSD bf16 bits or E4M3 codes
+    key_scales: np.ndarray | None
+    value: np.ndarray
+    value_scales: np.ndarray | None
+
+
+def kv_rope(kv, k_pe, *, H, d_nope, d_rope, d_v, cos, sin, fmt=FMT_BSHD, B=1, S=None,
+            cu_seqlens=None, out_dtype="mxfp8") -> KvResult:
+    """kv: bf16 [T, H, d_nope + d_v]; k_pe: bf16 [T, d_rope]."""
+    kvf = to_f64(kv)
+    pe = to_f64(k_pe)
+    T = kvf.shape[0]
+    if S is None:
+        S = T // B
+    pos, b, s = token_coords(fmt, T, B, S, cu_seqlens)
+    rot = rope_rotate(pe.reshape(T, 1, d_rope), pos, cos, sin, 0, d_rope)[:, 0, :]
+    key = np.concatenate([kvf[:, :, :d_nope], np.broadcast_to(rot[:, None, :], (T, H, d_rope))], axis=2)
+    val = kvf[:, :, d_nope:d_nope + d_v]
+    k32, v32 = key.astype(np.float32), val.astype(np.float32)
+    outs = []
+    for a32, D in ((k32, d_nope + d_rope), (v32, d_v)):
+        shape = out_shape(fmt, T, H, D, B, S)
+        if out_dtype == "bf16":
+            outs += [to_bhsd(f32_to_bf16_bits(a32), b, s, shape), None]
+        else:
+            codes, scales = mxfp8_quantize_blocks(a32)
+            outs += [to_bhsd(codes, b, s, shape), to_bhsd(scales, b, s, shape)]
+    return KvResult(k32, v32, *outs)

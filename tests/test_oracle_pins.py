@@ -584,3 +584,60 @@ def test_mx_backward_quantizes_the_stored_bf16_copy():
     assert o.bf16_bits_to_f64(r.dq_pre_bf16[1:2, dn:dn + 1])[0, 0] == 1.0625
     assert r.dq_rows[1][1, dn // 32] == 127 - 8
     assert r.dq_rows[0][1, dn] == 0x78
+
+
+# ------------------------------------------------------------ KV side ----
+def _kv_inputs(T, H, dn, dr, dv, seed):
+    rng = np.random.default_rng(seed)
+    kv = torch.from_numpy(rng.standard_normal((T, H, dn + dv)).astype(np.float32)).to(torch.bfloat16)
+    pe = torch.from_numpy(rng.standard_normal((T, dr)).astype(np.float32)).to(torch.bfloat16)
+    return kv, pe
+
+
+def test_kv_rope_passthrough_broadcast_and_closed_form():
+    # bf16 output: k_nope and v pass through bit for bit, every head carries the same
+    # rotated slice, position 0 is the identity, and at position p pair i is the closed
+    # form (a cos(p theta_i) - b sin(p theta_i), a sin(p theta_i) + b cos(p theta_i)).
+    T, H, dn, dr, dv = 5, 3, 32, 16, 32
+    kv, pe = _kv_inputs(T, H, dn, dr, dv, 11)
+    cos, sin = o.rope_table(T, dr, 10000.0)
+    r = o.kv_rope(kv, pe, H=H, d_nope=dn, d_rope=dr, d_v=dv, cos=cos, sin=sin, out_dtype="bf16")
+    kvb = kv.view(torch.int16).numpy().view(np.uint16)
+    key = r.key[0].transpose(1, 0, 2)      # [T, H, D] from BHSD with B = 1
+    val = r.value[0].transpose(1, 0, 2)
+    assert np.array_equal(key[:, :, :dn], kvb[:, :, :dn])
+    assert np.array_equal(val, kvb[:, :, dn:])
+    assert all(np.array_equal(key[:, h, dn:], key[:, 0, dn:]) for h in range(H))
+    peb = pe.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(key[0, 0, dn:], peb[0])
+    p, i = 3, 2
+    th = 10000.0 ** (-2 * i / dr)
+    a, b_ = o.to_f64(pe)[p, 2 * i], o.to_f64(pe)[p, 2 * i + 1]
+    want = (a * math.cos(p * th) - b_ * math.sin(p * th), a * math.sin(p * th) + b_ * math.cos(p * th))
+    got = r.key32[p, 1, dn + 2 * i:dn + 2 * i + 2]
+    assert np.allclose(got, want, rtol=1e-6, atol=1e-7)
+    # the rotated values are kept at float32 (no 16-bit rounding before quantization)
+    rope32 = r.key32[1:, 0, dn:]
+    assert (o.bf16_bits_to_f64(o.f32_to_bf16_bits(rope32)) != rope32).any()
+
+
+def test_kv_rope_mxfp8_blocks_and_bhsd_placement():
+    # MXFP8: key blocks of 32 along its head dim (one here spans k_nope and the rope
+    # slice), value blocks likewise; SBHD token order lands token t = s B + b at [b, :, s].
+    B, S, H, dn, dr, dv = 2, 3, 2, 16, 48, 64
+    T = B * S
+    kv, pe = _kv_inputs(T, H, dn, dr, dv, 12)
+    cos, sin = o.rope_table(S, dr, 10000.0)
+    r = o.kv_rope(kv, pe, H=H, d_nope=dn, d_rope=dr, d_v=dv, cos=cos, sin=sin, fmt=o.FMT_SBHD,
+                  B=B, S=S)
+    assert r.key.shape == (B, H, S, dn + dr) and r.key_scales.shape == (B, H, S, 2)
+    assert r.value.shape == (B, H, S, dv) and r.value_scales.shape == (B, H, S, 2)
+    t = 1 * B + 1   # s = 1, b = 1
+    for h in range(H):
+        blk = r.key32[t, h, :32]
+        e = o.floor_log2(np.abs(blk).max()) - 8
+        assert r.key_scales[1, h, 1, 0] == e + 127
+        deq = o.mxfp8_dequantize(r.key[1, h, 1], r.key_scales[1, h, 1])
+        assert np.all(np.abs(deq[:32] - blk) <= 2.0 ** -4 * np.abs(blk) + 2.0 ** (e - 10))
+    # the value is the kv tail, untouched before quantization
+    assert np.array_equal(r.value32, o.to_f64(kv)[:, :, dn:].astype(np.float32))
