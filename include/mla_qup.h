@@ -252,6 +252,35 @@ MLA_API mla_status mla_qup_bwd(const mla_qup_bwd_args* args, void* stream);
 MLA_API size_t mla_qup_bwd_mxfp8_workspace_size(const mla_qup_bwd_args* args);
 MLA_API mla_status mla_qup_bwd_mxfp8(const mla_qup_bwd_args* args, int32_t fp8_mfma, void* stream);
 
+/* KV side of the attention inputs. YaRN-fix page, Solution: the KV rotary
+ * writes fresh key and value outputs (nothing in place); forward page,
+ * flowchart: the key and the value each go through an MXFP8 quantization
+ * into the same BHSD scale layout as the query. Per token t and head h, with
+ * kv[t, h] = [k_nope | v] and one rope slice k_pe[t] shared by all heads:
+ *   key[t, h]   = [k_nope[t, h] | rotate(k_pe[t], pos_t)],  D_k = d_nope + d_rope
+ *   value[t, h] = v[t, h],                                 D_v = d_v
+ * rotated like the query (pairs (2i, 2i+1), (a, b) -> (a c - b s, a s + b c),
+ * fp32 from the bf16 inputs, quantized without a 16-bit rounding in between).
+ * A position with no table row gives NaN rope elements (an MXFP8 block
+ * holding one: scale 0xFF, codes 0x7F). */
+typedef struct {
+  const void* kv;           /* bf16 [T, H, d_nope + d_v] token-major; 16-B aligned */
+  const void* k_pe;         /* bf16 [T, d_rope]; 16-B aligned */
+  int32_t H, d_nope, d_rope, d_v;   /* H >= 1; each >= 0 and a multiple of 8;
+                                       D_k + D_v > 0 */
+  mla_tokens tokens;
+  mla_rope rope;            /* as the forward's (only read when d_rope > 0) */
+  int32_t out_dtype;        /* MLA_DTYPE_BF16 or MLA_DTYPE_MXFP8 (then D_k and
+                               D_v multiples of 32) */
+  void* key;                /* out: BHSD [B, H, S, D_k], bf16 or E4M3 codes; 16-B aligned */
+  void* key_scales;         /* out (MXFP8): E8M0 [B, H, S, D_k/32] */
+  void* value;              /* out: BHSD [B, H, S, D_v]; 16-B aligned */
+  void* value_scales;       /* out (MXFP8): E8M0 [B, H, S, D_v/32] */
+} mla_kv_args;
+
+/* Errors: MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EDEVICE. */
+MLA_API mla_status mla_kv_rope(const mla_kv_args* args, void* stream);
+
 /* Static string naming a status code. */
 MLA_API const char* mla_status_str(mla_status status);
 

@@ -23,7 +23,7 @@ FMT_BSHD, FMT_SBHD, FMT_THD = 0, 1, 2
 
 FUNCTIONS = ("rope_cache_build", "mxfp8_quantize", "mxfp8_quantize_t", "mla_qup_fwd", "mla_qup_bwd",
              "mla_qup_bwd_workspace_size", "mla_qup_bwd_mxfp8", "mla_qup_bwd_mxfp8_workspace_size",
-             "mla_status_str")
+             "mla_kv_rope", "mla_status_str")
 
 
 class mla_tokens(Structure):
@@ -47,6 +47,13 @@ class mla_qup_fwd_args(Structure):
                 ("d_rope", c_int32), ("tokens", mla_tokens), ("rope", mla_rope),
                 ("out_dtype", c_int32), ("out", c_void_p), ("out_scales", c_void_p),
                 ("flags", c_int32)]
+
+
+class mla_kv_args(Structure):
+    _fields_ = [("kv", c_void_p), ("k_pe", c_void_p), ("H", c_int32), ("d_nope", c_int32),
+                ("d_rope", c_int32), ("d_v", c_int32), ("tokens", mla_tokens), ("rope", mla_rope),
+                ("out_dtype", c_int32), ("key", c_void_p), ("key_scales", c_void_p),
+                ("value", c_void_p), ("value_scales", c_void_p)]
 
 
 class mla_qup_bwd_args(Structure):
@@ -82,10 +89,11 @@ def lib() -> ctypes.CDLL:
         L.mla_qup_bwd_mxfp8.argtypes = [POINTER(mla_qup_bwd_args), c_int32, c_void_p]
         L.mla_qup_bwd_mxfp8_workspace_size.argtypes = [POINTER(mla_qup_bwd_args)]
         L.mla_qup_bwd_mxfp8_workspace_size.restype = c_size_t
+        L.mla_kv_rope.argtypes = [POINTER(mla_kv_args), c_void_p]
         L.mla_status_str.argtypes = [c_int32]
         L.mla_status_str.restype = c_char_p
         for f in ("rope_cache_build", "mxfp8_quantize", "mxfp8_quantize_t", "mla_qup_fwd", "mla_qup_bwd",
-                  "mla_qup_bwd_mxfp8"):
+                  "mla_qup_bwd_mxfp8", "mla_kv_rope"):
             getattr(L, f).restype = c_int32
         _lib = L
     return _lib
@@ -260,3 +268,19 @@ def mla_qup_bwd_mxfp8(dq, x, w, dq_pre, *, fp8_mfma=False, stream=None, **kw):
     a = make_bwd_args(dq, x, w, dq_pre, **kw)
     _check(lib().mla_qup_bwd_mxfp8(ctypes.byref(a), 1 if fp8_mfma else 0, _stream(stream)),
            "mla_qup_bwd_mxfp8")
+
+
+def mla_kv_rope(kv, k_pe, key, value, *, H, d_nope, d_rope, d_v, cos=None, sin=None,
+                key_scales=None, value_scales=None, fmt=FMT_BSHD, B=1, S=None, cu_seqlens=None,
+                max_seqlen=None, stream=None):
+    """KV side: kv bf16 [T,H,d_nope+d_v], k_pe bf16 [T,d_rope] -> key [B,H,S,d_nope+d_rope]
+    and value [B,H,S,d_v] (BHSD; THD: B=1, S=T), bf16 or uint8 E4M3 codes with
+    key_scales / value_scales uint8 [.., D/32]."""
+    a = mla_kv_args()
+    a.kv, a.k_pe = _ptr(kv), _ptr(k_pe)
+    a.H, a.d_nope, a.d_rope, a.d_v = H, d_nope, d_rope, d_v
+    a.tokens = _tokens(kv.shape[0], fmt, B, S, cu_seqlens, max_seqlen)
+    a.rope = _rope(cos, sin, d_rope)
+    a.out_dtype = DTYPE_MXFP8 if key.dtype == torch.uint8 else DTYPE_BF16
+    a.key, a.key_scales, a.value, a.value_scales = _ptr(key), _ptr(key_scales), _ptr(value), _ptr(value_scales)
+    _check(lib().mla_kv_rope(ctypes.byref(a), _stream(stream)), "mla_kv_rope")

@@ -181,6 +181,67 @@ mla_status mxfp8_quantize_t(const void* x, int64_t rows, int64_t cols, int64_t l
                                                (hipStream_t)stream));
 }
 
+mla_status mla_kv_rope(const mla_kv_args* a, void* stream) {
+  if (a == nullptr) return MLA_EINVAL;
+  if (a->H < 1 || a->d_nope < 0 || a->d_rope < 0 || a->d_v < 0) return MLA_EINVAL;
+  if (a->d_nope % 8 || a->d_rope % 8 || a->d_v % 8 || a->d_nope + a->d_rope + a->d_v == 0) return MLA_EINVAL;
+  if (a->H > 65536 || a->d_nope + a->d_rope + a->d_v > 65536) return MLA_EINVAL;
+  if (a->out_dtype != MLA_DTYPE_BF16 && a->out_dtype != MLA_DTYPE_MXFP8) return MLA_EINVAL;
+  const bool mx = a->out_dtype == MLA_DTYPE_MXFP8;
+  const int Dk = a->d_nope + a->d_rope, Dv = a->d_v;
+  if (mx && (Dk % 32 || Dv % 32)) return MLA_EINVAL;
+  int64_t max_pos = 0;
+  mla_status st = check_tokens(a->tokens, &max_pos);
+  if (st) return st;
+  if ((st = check_rope(a->rope, a->d_rope, max_pos))) return st;
+  const int64_t T = a->tokens.T;
+  if (T == 0) return MLA_OK;
+  if (a->kv == nullptr || (Dk && a->key == nullptr) || (Dv && a->value == nullptr)) return MLA_EINVAL;
+  if (a->d_rope && a->k_pe == nullptr) return MLA_EINVAL;
+  if (mx && ((Dk && a->key_scales == nullptr) || (Dv && a->value_scales == nullptr))) return MLA_EINVAL;
+  if (!aligned(a->kv, 16) || !aligned(a->k_pe, 16) || !aligned(a->key, 16) || !aligned(a->value, 16))
+    return MLA_EINVAL;
+  const size_t eo = mx ? 1 : 2;
+  const size_t TH = (size_t)T * a->H;
+  std::vector<Range> ins = {rng(a->kv, TH * (a->d_nope + Dv) * 2)};
+  if (a->d_rope) {
+    ins.push_back(rng(a->k_pe, (size_t)T * a->d_rope * 2));
+    ins.push_back(rng(a->rope.cos, rope_bytes(a->rope, a->d_rope)));
+    ins.push_back(rng(a->rope.sin, rope_bytes(a->rope, a->d_rope)));
+  }
+  if (a->tokens.fmt == MLA_FMT_THD)
+    ins.push_back(rng(a->tokens.cu_seqlens, (size_t)(a->tokens.nseq + 1) * 4));
+  std::vector<Range> outs;
+  if (Dk) outs.push_back(rng(a->key, TH * Dk * eo));
+  if (Dv) outs.push_back(rng(a->value, TH * Dv * eo));
+  if (mx && Dk) outs.push_back(rng(a->key_scales, TH * Dk / 32));
+  if (mx && Dv) outs.push_back(rng(a->value_scales, TH * Dv / 32));
+  if (overlaps(outs, ins)) return MLA_EALIAS;
+  for (size_t i = 0; i < outs.size(); ++i)  // the outputs must not overlap each other either
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlaps({outs[i]}, {outs[j]})) return MLA_EALIAS;
+
+  mla::KvParams p{};
+  p.kv = (const uint16_t*)a->kv;
+  p.pe = (const uint16_t*)a->k_pe;
+  p.T = T;
+  p.H = a->H;
+  p.d_nope = a->d_nope;
+  p.d_rope = a->d_rope;
+  p.d_v = Dv;
+  fill_token_map(a->tokens, p.fmt, p.B, p.S, p.cu, p.nseq);
+  p.cos = a->rope.cos;
+  p.sin = a->rope.sin;
+  p.rope_rows = a->d_rope ? a->rope.rows : 0;
+  p.rope_pairs = a->d_rope ? a->rope.pairs : 0;
+  p.out_mx = mx;
+  p.key = a->key;
+  p.key_scales = (uint8_t*)a->key_scales;
+  p.value = a->value;
+  p.value_scales = (uint8_t*)a->value_scales;
+  return launched(mla::launch_kv_rope(p, (hipStream_t)stream));
+}
+
 mla_status mla_qup_fwd(const mla_qup_fwd_args* a, void* stream) {
   if (a == nullptr) return MLA_EINVAL;
   mla_status st = check_head_shape(a->K, a->H, a->d_nope, a->d_rope);

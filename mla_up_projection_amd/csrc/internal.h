@@ -83,6 +83,25 @@ int device_cu_count();
 
 hipError_t launch_rope_cache(float* cos, float* sin, int rows, int d_rope, double base,
                              const mla_yarn* yarn, hipStream_t stream);
+// KV side: fresh key = [k_nope | rotated k_pe] and value, BHSD, bf16 or MXFP8.
+struct KvParams {
+  const uint16_t* kv;      // bf16 [T, H, d_nope + d_v]
+  const uint16_t* pe;      // bf16 [T, d_rope]
+  int64_t T;
+  int H, d_nope, d_rope, d_v;
+  int fmt, B, S;
+  const int32_t* cu;
+  int nseq;
+  const float* cos;
+  const float* sin;
+  int rope_rows, rope_pairs;
+  int out_mx;
+  void* key;               // [B, H, S, d_nope + d_rope]
+  uint8_t* key_scales;     // [B, H, S, (d_nope + d_rope) / 32]
+  void* value;             // [B, H, S, d_v]
+  uint8_t* value_scales;   // [B, H, S, d_v / 32]
+};
+hipError_t launch_kv_rope(const KvParams& p, hipStream_t stream);
 hipError_t launch_mxfp8_quantize_t(const void* x, int64_t rows, int64_t cols, int64_t ld, int64_t rows_pad,
                                    uint8_t* codes_t, uint8_t* scales_t, hipStream_t stream);
 hipError_t launch_mxfp8_quantize(const void* x, int x_fp32, int64_t rows, int64_t cols,

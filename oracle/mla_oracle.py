@@ -478,6 +478,7 @@ def qup_backward_mxfp8(dq, x, w, *, H, d_nope, d_rope, cos, sin, fmt=FMT_BSHD, B
 # ---------------------------------------------------------------------------
 @dataclass
 class KvResult:
+    key64: np.ndarray            # float64 [T, H, d_nope + d_rope], token-major, exact
     key32: np.ndarray            # float32 [T, H, d_nope + d_rope], token-major
     value32: np.ndarray          # float32 [T, H, d_v]
     key: np.ndarray              # BHSD bf16 bits or E4M3 codes
@@ -507,4 +508,4 @@ def kv_rope(kv, k_pe, *, H, d_nope, d_rope, d_v, cos, sin, fmt=FMT_BSHD, B=1, S=
         else:
             codes, scales = mxfp8_quantize_blocks(a32)
             outs += [to_bhsd(codes, b, s, shape), to_bhsd(scales, b, s, shape)]
-    return KvResult(k32, v32, *outs)
+    return KvResult(key, k32, v32, *outs)

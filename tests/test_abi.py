@@ -44,7 +44,8 @@ def test_status_strings(L):
 
 def test_struct_layouts_match_c(tmp_path):
     """sizeof/offsetof of every ABI struct as gcc lays it out == the ctypes mirror."""
-    structs = [bd.mla_tokens, bd.mla_yarn, bd.mla_rope, bd.mla_qup_fwd_args, bd.mla_qup_bwd_args]
+    structs = [bd.mla_tokens, bd.mla_yarn, bd.mla_rope, bd.mla_qup_fwd_args, bd.mla_qup_bwd_args,
+               bd.mla_kv_args]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "mla_qup.h"', "int main(void){"]
     for s in structs:
         lines.append(f'printf("{s.__name__} %zu\\n", sizeof({s.__name__}));')
@@ -208,6 +209,52 @@ def test_quantize_t_validation(L):
     assert q(addr(1, 8), 40, 64, 64, 64, addr(2), addr(3), None) == bd.MLA_EINVAL  # x alignment
     assert q(addr(1), 40, 64, 64, 64, addr(1, 256), addr(3), None) == bd.MLA_EALIAS
     assert q(addr(1), 0, 64, 64, 0, 0, 0, None) == bd.MLA_OK
+
+
+def kv_args(**over):
+    a = bd.mla_kv_args()
+    T, H, dn, dr, dv = 256, 4, 128, 64, 128
+    a.kv, a.k_pe = addr(1), addr(2)
+    a.H, a.d_nope, a.d_rope, a.d_v = H, dn, dr, dv
+    a.tokens.fmt, a.tokens.B, a.tokens.S, a.tokens.T = bd.FMT_BSHD, 1, T, T
+    a.rope.cos, a.rope.sin, a.rope.rows, a.rope.pairs = addr(3), addr(4), T, dr // 2
+    a.out_dtype = bd.DTYPE_MXFP8
+    a.key, a.key_scales, a.value, a.value_scales = addr(5), addr(6), addr(7), addr(8)
+    for k, v in over.items():
+        obj = a
+        *path, last = k.split("__")
+        for p in path:
+            obj = getattr(obj, p)
+        setattr(obj, last, v)
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(H=0), bd.MLA_EINVAL),
+    (dict(d_nope=12), bd.MLA_EINVAL),                   # not a multiple of 8
+    (dict(d_nope=0, d_rope=0, d_v=0), bd.MLA_EINVAL),
+    (dict(d_v=48), bd.MLA_EINVAL),                      # MXFP8 needs whole 32-blocks
+    (dict(out_dtype=7), bd.MLA_EINVAL),
+    (dict(rope__pairs=16), bd.MLA_EROPE_TABLE),
+    (dict(rope__rows=100), bd.MLA_EROPE_TABLE),
+    (dict(k_pe=0), bd.MLA_EINVAL),
+    (dict(key_scales=0), bd.MLA_EINVAL),
+    (dict(kv=addr(1, 8)), bd.MLA_EINVAL),               # alignment
+    (dict(key=addr(1, 1024)), bd.MLA_EALIAS),            # key inside kv
+    (dict(value=addr(5, 4096)), bd.MLA_EALIAS),          # value inside key
+    (dict(value_scales=addr(2, 64)), bd.MLA_EALIAS),     # scales inside k_pe
+    (dict(tokens__T=0, tokens__S=1, tokens__B=1), bd.MLA_EINVAL),  # B*S != T
+])
+def test_kv_rope_validation(L, over, code):
+    assert L.mla_kv_rope(ctypes.byref(kv_args(**over)), None) == code
+
+
+def test_kv_rope_zero_tokens_and_bf16_widths(L):
+    thd = dict(tokens__fmt=bd.FMT_THD, tokens__cu_seqlens=addr(9), tokens__nseq=1,
+               tokens__max_seqlen=8, tokens__T=0)
+    assert L.mla_kv_rope(ctypes.byref(kv_args(**thd)), None) == bd.MLA_OK
+    # bf16 output needs only multiples of 8
+    assert L.mla_kv_rope(ctypes.byref(kv_args(**thd, out_dtype=bd.DTYPE_BF16, d_v=40)), None) == bd.MLA_OK
 
 
 def test_rope_and_quantize_validation(L):

@@ -655,3 +655,92 @@ def test_bwd_mxfp8_full_size_sampled():
         lim = 2.0 ** -9 * 1.1 + (1e-3 if fp8 else 0.0)
         assert ex <= lim and ew <= lim
         assert frob_rel(o.to_f64(g["db"].cpu()), ref[2]) <= 1e-2
+
+
+# ------------------------------------------------------------ KV side ------
+U32 = 2.0 ** -24
+
+
+def kv_bound(pe64, cos, sin, pos, H, dn, dv):
+    """float32 error bound of the rotated key elements (two products and a sum
+    per element, doubled); the k_nope and value elements are exact copies."""
+    T, dr = pe64.shape
+    a, b = np.abs(pe64[:, 0::2]), np.abs(pe64[:, 1::2])
+    c, s = np.abs(cos[pos].astype(np.float64)), np.abs(sin[pos].astype(np.float64))
+    e = 8 * U32 * (a + b) * (c + s)
+    rot = np.repeat(e, 2, axis=1)
+    key = np.concatenate([np.zeros((T, H, dn)), np.broadcast_to(rot[:, None, :], (T, H, dr))], axis=2)
+    return key
+
+
+def run_kv(kv, pe, *, H, dn, dr, dv, mx, fmt=m.FMT_BSHD, B=1, S=None, cu=None, max_seqlen=None,
+           cos=None, sin=None):
+    T = kv.shape[0]
+    S = S if S is not None else T // B
+    Bo, So = (1, T) if fmt == m.FMT_THD else (B, S)
+    dt = torch.uint8 if mx else torch.bfloat16
+    key = torch.empty(Bo, H, So, dn + dr, dtype=dt, device=DEV)
+    val = torch.empty(Bo, H, So, dv, dtype=dt, device=DEV)
+    ks = torch.empty(Bo, H, So, (dn + dr) // 32, dtype=torch.uint8, device=DEV) if mx else None
+    vs = torch.empty(Bo, H, So, dv // 32, dtype=torch.uint8, device=DEV) if mx else None
+    m.mla_kv_rope(_dev(kv), _dev(pe), key, val, H=H, d_nope=dn, d_rope=dr, d_v=dv, cos=cos, sin=sin,
+                  key_scales=ks, value_scales=vs, fmt=fmt, B=B, S=S,
+                  cu_seqlens=_dev(cu) if cu is not None else None, max_seqlen=max_seqlen)
+    torch.cuda.synchronize()
+    return key, val, ks, vs
+
+
+@pytest.mark.parametrize("fmt,B,S,lengths", [(m.FMT_BSHD, 1, 333, None), (m.FMT_SBHD, 3, 77, None),
+                                             (m.FMT_THD, 1, None, [64, 129, 7])])
+def test_kv_rope_against_oracle(fmt, B, S, lengths):
+    H, dn, dr, dv = 3, 128, 64, 128
+    cu = syn.cu_seqlens_of(lengths) if lengths else None
+    T = sum(lengths) if lengths else B * S
+    max_pos = max(lengths) if lengths else S
+    kv = syn.normal_bf16((T, H, dn + dv), 1.0, 180)
+    pe = syn.normal_bf16((T, dr), 1.0, 181)
+    cos, sin, oc, os_ = rope_tables(max_pos, dr)
+    okw = dict(H=H, d_nope=dn, d_rope=dr, d_v=dv, cos=oc, sin=os_, fmt=fmt, B=B, S=S,
+               cu_seqlens=cu.numpy() if cu is not None else None)
+    gkw = dict(H=H, dn=dn, dr=dr, dv=dv, fmt=fmt, B=B, S=S, cu=cu, max_seqlen=max_pos, cos=cos, sin=sin)
+    # bf16 outputs: k_nope and value are copies (bit-exact), the rope slice within bf16 rounding
+    key, val, _, _ = run_kv(kv, pe, mx=False, **gkw)
+    r = o.kv_rope(kv, pe, out_dtype="bf16", **okw)
+    kb, vb = bits16(key), bits16(val)
+    assert np.array_equal(vb, r.value)
+    assert np.array_equal(kb[..., :dn], r.key[..., :dn])
+    check_bf16(kb, r.key, "kv key bf16")
+    # MXFP8 outputs
+    key, val, ks, vs = run_kv(kv, pe, mx=True, **gkw)
+    r = o.kv_rope(kv, pe, **okw)
+    pos, bb, ss = o.token_coords(fmt, T, B, S if S else T, okw["cu_seqlens"])
+    bnd = kv_bound(o.to_f64(pe), oc, os_, pos, H, dn, dv)
+    g = key.cpu().numpy()[bb, :, ss, :]          # back to token-major [T, H, D]
+    gs = ks.cpu().numpy()[bb, :, ss, :]
+    stats = check_mx(g, gs, r.key64, 2 * bnd + U32 * np.abs(r.key64), "kv key mxfp8")
+    assert np.array_equal(val.cpu().numpy(), r.value) and np.array_equal(vs.cpu().numpy(), r.value_scales)
+    print(f"\nkv {fmt}: {stats}", flush=True)
+
+
+def test_kv_rope_dsv3_sampled():
+    """DeepSeek-V3 KV side: T = 4096, 128 heads of [128 k_nope | 128 v], a 64-wide
+    shared rope slice, MXFP8 outputs; sampled tokens against the oracle (the
+    sampled rows as a batch of one sequence of positions `rows`, with the
+    table re-indexed to those positions)."""
+    T, H, dn, dr, dv = 4096, 128, 128, 64, 128
+    kv = syn.normal_bf16((T, H, dn + dv), 1.0, 190)
+    pe = syn.normal_bf16((T, dr), 1.0, 191)
+    cos, sin, oc, os_ = rope_tables(T, dr)
+    key, val, ks, vs = run_kv(kv, pe, H=H, dn=dn, dr=dr, dv=dv, mx=True, S=T, cos=cos, sin=sin)
+    rows = sample_rows(T)
+    n = len(rows)
+    r = o.kv_rope(kv[rows], pe[rows], H=H, d_nope=dn, d_rope=dr, d_v=dv, cos=oc[rows], sin=os_[rows],
+                  B=1, S=n)
+    bnd = kv_bound(o.to_f64(pe[rows]), oc[rows], os_[rows], np.arange(n), H, dn, dv)
+    ri = torch.from_numpy(rows).to(DEV)
+    g = key[0][:, ri, :].permute(1, 0, 2).cpu().numpy()
+    gs = ks[0][:, ri, :].permute(1, 0, 2).cpu().numpy()
+    stats = check_mx(g, gs, r.key64, 2 * bnd + U32 * np.abs(r.key64), "kv dsv3 key")
+    assert np.array_equal(val[0][:, ri, :].cpu().numpy(), r.value[0])
+    assert np.array_equal(vs[0][:, ri, :].cpu().numpy(), r.value_scales[0])
+    print(f"\nkv dsv3: {stats}", flush=True)
