@@ -236,6 +236,21 @@ def main():
     parts["qup_fwd_thd_yarn_16384"] = {"ms": ms4, "tflops": tf4, "pct_bf16_peak": 100 * tf4 / BF16_PEAK_TFLOPS,
                                        "sequences": len(w4.lengths)}
     del x4, out4
+    # KV side at DeepSeek-V3: 128 heads of [128 k_nope | 128 v], 64-wide shared
+    # rope slice, MXFP8 key and value in BHSD (one HBM pass)
+    dv = 128
+    kvin = syn.normal_bf16((T, H, dn + dv), 1.0, 190).to(dev)
+    kpe = syn.normal_bf16((T, dr), 1.0, 191).to(dev)
+    kkey = torch.empty(1, H, T, dn + dr, dtype=torch.uint8, device=dev)
+    kks = torch.empty(1, H, T, (dn + dr) // 32, dtype=torch.uint8, device=dev)
+    kval = torch.empty(1, H, T, dv, dtype=torch.uint8, device=dev)
+    kvs = torch.empty(1, H, T, dv // 32, dtype=torch.uint8, device=dev)
+    ms_kv = timed(lambda: m.mla_kv_rope(kvin, kpe, kkey, kval, H=H, d_nope=dn, d_rope=dr, d_v=dv,
+                                        cos=cos, sin=sin, key_scales=kks, value_scales=kvs, B=1, S=T), R)
+    kv_bytes = T * H * (dn + dv) * 2 + T * dr * 2 + T * H * (dn + dr + dv) * (1 + 1 / 32)
+    parts["kv_rope_mxfp8_dsv3"] = {"ms": ms_kv, "gbs": kv_bytes / (ms_kv * 1e-3) / 1e9,
+                                   "pct_hbm_peak": 100 * kv_bytes / (ms_kv * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del kvin, kpe, kkey, kks, kval, kvs
     # context: the vendor library GEMM (torch -> hipBLASLt) on the same three
     # products, bf16 out, with no epilogue and no inverse RoPE
     dq2 = dq.reshape(T, N)

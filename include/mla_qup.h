@@ -267,7 +267,7 @@ typedef struct {
   const void* kv;           /* bf16 [T, H, d_nope + d_v] token-major; 16-B aligned */
   const void* k_pe;         /* bf16 [T, d_rope]; 16-B aligned */
   int32_t H, d_nope, d_rope, d_v;   /* H >= 1; each >= 0 and a multiple of 8;
-                                       D_k + D_v > 0 */
+                                       d_rope <= 256; D_k + D_v > 0 */
   mla_tokens tokens;
   mla_rope rope;            /* as the forward's (only read when d_rope > 0) */
   int32_t out_dtype;        /* MLA_DTYPE_BF16 or MLA_DTYPE_MXFP8 (then D_k and
@@ -278,7 +278,8 @@ typedef struct {
   void* value_scales;       /* out (MXFP8): E8M0 [B, H, S, D_v/32] */
 } mla_kv_args;
 
-/* Errors: MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EDEVICE. */
+/* Errors: MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EDEVICE;
+ * MLA_EUNSUPPORTED when T*H*(D_k + D_v)/8 exceeds 2^31 - 1. */
 MLA_API mla_status mla_kv_rope(const mla_kv_args* args, void* stream);
 
 /* Static string naming a status code. */

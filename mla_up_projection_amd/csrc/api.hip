@@ -185,7 +185,7 @@ mla_status mla_kv_rope(const mla_kv_args* a, void* stream) {
   if (a == nullptr) return MLA_EINVAL;
   if (a->H < 1 || a->d_nope < 0 || a->d_rope < 0 || a->d_v < 0) return MLA_EINVAL;
   if (a->d_nope % 8 || a->d_rope % 8 || a->d_v % 8 || a->d_nope + a->d_rope + a->d_v == 0) return MLA_EINVAL;
-  if (a->H > 65536 || a->d_nope + a->d_rope + a->d_v > 65536) return MLA_EINVAL;
+  if (a->H > 65536 || a->d_nope + a->d_rope + a->d_v > 65536 || a->d_rope > 256) return MLA_EINVAL;
   if (a->out_dtype != MLA_DTYPE_BF16 && a->out_dtype != MLA_DTYPE_MXFP8) return MLA_EINVAL;
   const bool mx = a->out_dtype == MLA_DTYPE_MXFP8;
   const int Dk = a->d_nope + a->d_rope, Dv = a->d_v;
@@ -196,6 +196,7 @@ mla_status mla_kv_rope(const mla_kv_args* a, void* stream) {
   if ((st = check_rope(a->rope, a->d_rope, max_pos))) return st;
   const int64_t T = a->tokens.T;
   if (T == 0) return MLA_OK;
+  if (T * a->H * ((Dk + Dv) / 8) > (int64_t)INT32_MAX) return MLA_EUNSUPPORTED;  // 32-bit unit index
   if (a->kv == nullptr || (Dk && a->key == nullptr) || (Dv && a->value == nullptr)) return MLA_EINVAL;
   if (a->d_rope && a->k_pe == nullptr) return MLA_EINVAL;
   if (mx && ((Dk && a->key_scales == nullptr) || (Dv && a->value_scales == nullptr))) return MLA_EINVAL;

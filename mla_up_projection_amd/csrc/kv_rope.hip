@@ -10,83 +10,135 @@
 // with kv[t, h] = [k_nope | v]. HBM-bound: each kv element is read once and
 // each output element written once (2 bytes, or 1 + 1/32 for MXFP8).
 //
-// One thread owns 8 consecutive output elements of one (t, h) row of
-// [key | value] (one 16-byte load of kv or k_pe); for MXFP8 the four threads
-// of a 32-element block are lanes 4j .. 4j + 3 and share the block amax
-// through two xor-shuffles, as in the row quantizer.
+// One thread owns one 32-element block (or 8 elements for bf16 widths that
+// are not multiples of 32) of one (t, h) row of [key | value].
 #include "device_common.h"
 #include "internal.h"
 
 namespace mla {
 namespace {
 
+constexpr int KV_TOK = 8;         // tokens per workgroup chunk
+constexpr int KV_MAX_ROPE = 256;  // widest rope slice (the ABI limits d_rope to this)
+
+// A workgroup owns KV_TOK consecutive tokens, all heads. It first rotates
+// the tokens' shared k_pe slices once into LDS (with the tokens' BHSD
+// coordinates), then each thread takes EPT consecutive output elements of one
+// (t, h) row of [key | value]: 32 (one whole MXFP8 block, amax in the thread)
+// when both widths are multiples of 32, else 8 (bf16 output). The kv loads
+// (16 bytes each) of a unit are issued before any arithmetic; rope elements
+// come from LDS.
+template <int EPT>
 __global__ __launch_bounds__(256) void kv_rope_kernel(KvParams p) {
+  constexpr int NG = EPT / 8;
+  __shared__ float rot[KV_TOK * KV_MAX_ROPE];
+  __shared__ int64_t orow0[KV_TOK];  // BHSD row of head 0: (b H) S + s
   const int Dk = p.d_nope + p.d_rope;
   const int row_in = p.d_nope + p.d_v;
-  const int gpr = (Dk + p.d_v) / 8;  // 8-element groups per (t, h) row
-  const int64_t groups = p.T * p.H * gpr;
+  const int upr = (Dk + p.d_v) / EPT;  // units per (t, h) row
+  const int per_tok = p.H * upr;
+  const int64_t HS = (int64_t)p.H * p.S;
   const TokenMap tm{p.fmt, p.B, p.S, p.cu, p.nseq};
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
-    const int64_t row = g / gpr;
-    const int e = (int)(g - row * gpr) * 8;
-    const int64_t t = row / p.H;
-    const int h = (int)(row - t * p.H);
-    int pos, b, s;
-    token_coords(tm, t, pos, b, s);
-    float v[8];
-    const bool is_key = e < Dk;
-    const int d = is_key ? e : e - Dk;
-    if (is_key && d >= p.d_nope) {
-      // rope slice: pairs j/2 .. j/2 + 3 of the token's shared k_pe
-      const int j = d - p.d_nope;
-      const uint4 u = *reinterpret_cast<const uint4*>(p.pe + t * p.d_rope + j);
-      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-      const bool pos_ok = pos >= 0 && pos < p.rope_rows;
-      const int64_t trow = (int64_t)(pos_ok ? pos : 0) * p.rope_pairs + j / 2;
-      const float nan = __builtin_nanf("");
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = bf16_bits_to_f32(wv[i] & 0xFFFFu), bb = bf16_bits_to_f32(wv[i] >> 16);
-        const float c = pos_ok ? p.cos[trow + i] : nan, sn = pos_ok ? p.sin[trow + i] : nan;
-        v[2 * i] = a * c - bb * sn;
-        v[2 * i + 1] = a * sn + bb * c;
-      }
-    } else {
-      const int src = is_key ? d : p.d_nope + d;
-      const uint4 u = *reinterpret_cast<const uint4*>(p.kv + row * row_in + src);
-      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_bits_to_f32(wv[i] & 0xFFFFu);
-        v[2 * i + 1] = bf16_bits_to_f32(wv[i] >> 16);
+  const int chunks = (int)((p.T + KV_TOK - 1) / KV_TOK);
+  for (int ck = blockIdx.x; ck < chunks; ck += gridDim.x) {
+    const int t0 = ck * KV_TOK;
+    const int nt = min(KV_TOK, (int)p.T - t0);
+    __syncthreads();  // the previous chunk's readers of rot / orow0 are done
+    for (int i = threadIdx.x; i < nt * (p.d_rope / 2 + 1); i += blockDim.x) {
+      const int tl = i / (p.d_rope / 2 + 1);
+      const int k = i - tl * (p.d_rope / 2 + 1);  // pair k, or the coordinates at k == d_rope/2
+      int pos, b, s;
+      token_coords(tm, t0 + tl, pos, b, s);
+      if (k == p.d_rope / 2) {
+        orow0[tl] = (int64_t)b * HS + s;
+      } else {
+        const uint32_t ab = *reinterpret_cast<const uint32_t*>(p.pe + (int64_t)(t0 + tl) * p.d_rope + 2 * k);
+        const float a = bf16_bits_to_f32(ab & 0xFFFFu), bb = bf16_bits_to_f32(ab >> 16);
+        const bool ok = pos >= 0 && pos < p.rope_rows;
+        const float nan = __builtin_nanf("");
+        const int64_t ti = (int64_t)(ok ? pos : 0) * p.rope_pairs + k;
+        const float c = ok ? p.cos[ti] : nan, sn = ok ? p.sin[ti] : nan;
+        rot[tl * KV_MAX_ROPE + 2 * k] = a * c - bb * sn;
+        rot[tl * KV_MAX_ROPE + 2 * k + 1] = a * sn + bb * c;
       }
     }
-    const int D = is_key ? Dk : p.d_v;
-    const int64_t orow = ((int64_t)b * p.H + h) * p.S + s;  // BHSD (b, h, s)
-    if (!p.out_mx) {
-      uint16_t* dst = static_cast<uint16_t*>(is_key ? p.key : p.value) + orow * D + d;
-      *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-    } else {
-      uint32_t m = 0;
+    __syncthreads();
+    const int n = nt * per_tok;
+    // two units per thread per pass: both units' kv loads are in flight together
+    for (int i0 = threadIdx.x; i0 < n; i0 += 2 * blockDim.x) {
+      int tl[2], h[2], d0[2];
+      bool key[2], live[2];
+      uint4 raw[2][NG];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = max(m, abs_bits(v[i]));
-      m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-      m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-      uint32_t c0, c1, sc;
-      if (m >= 0x7F800000u) {
-        c0 = c1 = 0x7F7F7F7Fu;
-        sc = 0xFF;
-      } else {
-        const int E = mx_block_exp(m);
-        c0 = e4m3_pack4(v[0], v[1], v[2], v[3], E);
-        c1 = e4m3_pack4(v[4], v[5], v[6], v[7], E);
-        sc = (uint32_t)(E + 127);
+      for (int w = 0; w < 2; ++w) {
+        const int i = i0 + w * blockDim.x;
+        live[w] = i < n;
+        const int ii = live[w] ? i : i0;
+        tl[w] = ii / per_tok;
+        const int rem = ii - tl[w] * per_tok;
+        h[w] = rem / upr;
+        const int e0 = (rem - h[w] * upr) * EPT;
+        key[w] = e0 < Dk;
+        d0[w] = key[w] ? e0 : e0 - Dk;
+        const int64_t row = (int64_t)(t0 + tl[w]) * p.H + h[w];  // kv row (t, h)
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+          const int d = d0[w] + 8 * q;
+          if (!(key[w] && d >= p.d_nope))
+            raw[w][q] = *reinterpret_cast<const uint4*>(p.kv + row * row_in + (key[w] ? d : p.d_nope + d));
+        }
       }
-      uint8_t* dst = static_cast<uint8_t*>(is_key ? p.key : p.value) + orow * D + d;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(c0, c1);
-      if ((d & 31) == 0) (is_key ? p.key_scales : p.value_scales)[orow * (D / 32) + d / 32] = (uint8_t)sc;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        if (!live[w]) continue;
+        float v[EPT];
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+          const int d = d0[w] + 8 * q;
+          if (key[w] && d >= p.d_nope) {
+            const float* r = rot + tl[w] * KV_MAX_ROPE + (d - p.d_nope);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[8 * q + k] = r[k];
+          } else {
+            const uint32_t wv[4] = {raw[w][q].x, raw[w][q].y, raw[w][q].z, raw[w][q].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              v[8 * q + 2 * k] = bf16_bits_to_f32(wv[k] & 0xFFFFu);
+              v[8 * q + 2 * k + 1] = bf16_bits_to_f32(wv[k] >> 16);
+            }
+          }
+        }
+        const bool is_key = key[w];
+        const int D = is_key ? Dk : p.d_v;
+        const int64_t orow = orow0[tl[w]] + (int64_t)h[w] * p.S;  // BHSD (b, h, s)
+        if (!p.out_mx) {
+          uint16_t* dst = static_cast<uint16_t*>(is_key ? p.key : p.value) + orow * D + d0[w];
+#pragma unroll
+          for (int q = 0; q < NG; ++q)
+            reinterpret_cast<uint4*>(dst)[q] =
+                make_uint4(pack_bf16x2(v[8 * q], v[8 * q + 1]), pack_bf16x2(v[8 * q + 2], v[8 * q + 3]),
+                           pack_bf16x2(v[8 * q + 4], v[8 * q + 5]), pack_bf16x2(v[8 * q + 6], v[8 * q + 7]));
+        } else if (EPT == 32) {
+          uint32_t m = 0;
+#pragma unroll
+          for (int k = 0; k < EPT; ++k) m = max(m, abs_bits(v[k]));
+          uint32_t c[8], sc;
+          if (m >= 0x7F800000u) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c[k] = 0x7F7F7F7Fu;
+            sc = 0xFF;
+          } else {
+            const int E = mx_block_exp(m);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c[k] = e4m3_pack4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3], E);
+            sc = (uint32_t)(E + 127);
+          }
+          uint8_t* dst = static_cast<uint8_t*>(is_key ? p.key : p.value) + orow * D + d0[w];
+          reinterpret_cast<uint4*>(dst)[0] = make_uint4(c[0], c[1], c[2], c[3]);
+          reinterpret_cast<uint4*>(dst)[1] = make_uint4(c[4], c[5], c[6], c[7]);
+          (is_key ? p.key_scales : p.value_scales)[orow * (D / 32) + d0[w] / 32] = (uint8_t)sc;
+        }
+      }
     }
   }
 }
@@ -94,11 +146,16 @@ __global__ __launch_bounds__(256) void kv_rope_kernel(KvParams p) {
 }  // namespace
 
 hipError_t launch_kv_rope(const KvParams& p, hipStream_t stream) {
-  const int64_t groups = p.T * p.H * ((p.d_nope + p.d_rope + p.d_v) / 8);
-  int64_t blocks = (groups + 255) / 256;
-  if (blocks > 16384) blocks = 16384;
+  const int W = p.d_nope + p.d_rope + p.d_v;
+  const bool whole = (p.d_nope + p.d_rope) % 32 == 0 && p.d_v % 32 == 0;  // always so for MXFP8
+  (void)W;
+  int64_t blocks = (p.T + KV_TOK - 1) / KV_TOK;
+  if (blocks > 65535) blocks = 65535;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(kv_rope_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  if (whole)
+    hipLaunchKernelGGL(kv_rope_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(kv_rope_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
