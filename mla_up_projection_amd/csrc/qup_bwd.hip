@@ -35,7 +35,12 @@ constexpr int IR_THREADS = 128;
 constexpr int IR_COLS = IR_THREADS * 8;  // columns per workgroup
 constexpr int IR_ROWS = 64;              // token rows per workgroup
 
-__global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, float* __restrict__ db_part) {
+// RQ: also quantize each dq_pre row along n from its bf16 copy (the MXFP8
+// backward's dX operand): the four lanes of a 32-column block share its amax
+// through two xor-shuffles; codes [T, N] and scales [T, N/32].
+template <bool RQ>
+__global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, float* __restrict__ db_part,
+                                                              uint8_t* __restrict__ rc, uint8_t* __restrict__ rs) {
   __shared__ int s_pos[IR_ROWS];
   const int64_t r0 = (int64_t)blockIdx.y * IR_ROWS;
   const int rows = (int)min((int64_t)IR_ROWS, p.T - r0);
@@ -119,6 +124,32 @@ __global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, float
         o[k] = pack_bf16x2(a, b);
       }
       *reinterpret_cast<u32x4_t*>(dq_pre + (r0 + i0 + j) * p.N + n0) = u32x4_t{o[0], o[1], o[2], o[3]};
+      if (RQ) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[2 * k] = bf16_bits_to_f32(o[k] & 0xFFFFu);
+          v[2 * k + 1] = bf16_bits_to_f32(o[k] >> 16);
+        }
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = max(m, abs_bits(v[k]));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+        uint32_t c0, c1, sc;
+        if (m >= 0x7F800000u) {
+          c0 = c1 = 0x7F7F7F7Fu;
+          sc = 0xFF;
+        } else {
+          const int E = mx_block_exp(m);
+          c0 = e4m3_pack4(v[0], v[1], v[2], v[3], E);
+          c1 = e4m3_pack4(v[4], v[5], v[6], v[7], E);
+          sc = (uint32_t)(E + 127);
+        }
+        const int64_t row = r0 + i0 + j;
+        *reinterpret_cast<uint2*>(rc + row * p.N + n0) = make_uint2(c0, c1);
+        if ((threadIdx.x & 3) == 0) rs[row * (p.N / 32) + n0 / 32] = (uint8_t)sc;
+      }
     }
   }
   if (db_part) {
@@ -642,7 +673,7 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
   float* db_part = p.use_bias ? reinterpret_cast<float*>(ws + pl.db_off) : nullptr;
   {
     dim3 grid((p.N + IR_COLS - 1) / IR_COLS, pl.db_row_chunks);
-    hipLaunchKernelGGL(inv_rope_kernel, grid, dim3(IR_THREADS), 0, stream, p, db_part);
+    hipLaunchKernelGGL(inv_rope_kernel<false>, grid, dim3(IR_THREADS), 0, stream, p, db_part, nullptr, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -770,17 +801,21 @@ MxBwdPlan plan_bwd_mx(int64_t T, int N, int K, bool use_bias) {
 hipError_t launch_qup_bwd_mx(const BwdParams& p, const MxBwdPlan& pl, int fp8_mfma, hipStream_t stream) {
   if (p.T == 0) return launch_qup_bwd(p, pl.base, stream);  // zero dW and db
   uint8_t* ws = static_cast<uint8_t*>(p.workspace);
-  // dq_pre and db exactly as the bf16 backward (no dX / dW products there)
-  BwdParams q = p;
-  q.dx = nullptr;
-  q.dw = nullptr;
-  hipError_t e = launch_qup_bwd(q, pl.base, stream);
-  if (e != hipSuccess) return e;
   const int64_t T = p.T;
   const int N = p.N, K = p.K;
+  // dq_pre with its quantization along n (the dX operand) and the db partials
+  // in one pass; the quantization along t reads the stored dq_pre below
+  float* db_part = p.use_bias ? reinterpret_cast<float*>(ws + pl.base.db_off) : nullptr;
+  hipLaunchKernelGGL(inv_rope_kernel<true>, dim3((N + IR_COLS - 1) / IR_COLS, pl.base.db_row_chunks),
+                     dim3(IR_THREADS), 0, stream, p, db_part, ws + pl.dq_rows, ws + pl.dq_rows_sc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.use_bias) {
+    hipLaunchKernelGGL(db_reduce_kernel, dim3((N + DBR_COLS - 1) / DBR_COLS), dim3(256), 0, stream, db_part,
+                       pl.base.db_row_chunks, N, p.db);
+    if ((e = hipGetLastError())) return e;
+  }
   if (p.dx) {
-    if ((e = launch_mxfp8_quantize(p.dq_pre, 0, T, N, N, ws + pl.dq_rows, ws + pl.dq_rows_sc, stream)))
-      return e;
     if ((e = launch_mxfp8_quantize_t(p.w, N, K, K, N, ws + pl.w_t, ws + pl.w_t_sc, stream))) return e;
     FwdParams g{};
     g.x = ws + pl.dq_rows;
