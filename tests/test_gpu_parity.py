@@ -744,3 +744,17 @@ def test_kv_rope_dsv3_sampled():
     assert np.array_equal(val[0][:, ri, :].cpu().numpy(), r.value[0])
     assert np.array_equal(vs[0][:, ri, :].cpu().numpy(), r.value_scales[0])
     print(f"\nkv dsv3: {stats}", flush=True)
+
+
+def test_kv_rope_bf16_widths_not_multiple_of_32():
+    """bf16 output with k_nope 24, rope 16, value 40 (8-element units)."""
+    T, H, dn, dr, dv = 100, 2, 24, 16, 40
+    kv = syn.normal_bf16((T, H, dn + dv), 1.0, 200)
+    pe = syn.normal_bf16((T, dr), 1.0, 201)
+    cos, sin, oc, os_ = rope_tables(T, dr)
+    key, val, _, _ = run_kv(kv, pe, H=H, dn=dn, dr=dr, dv=dv, mx=False, S=T, cos=cos, sin=sin)
+    r = o.kv_rope(kv, pe, H=H, d_nope=dn, d_rope=dr, d_v=dv, cos=oc, sin=os_, S=T, out_dtype="bf16")
+    kb = bits16(key)
+    assert np.array_equal(bits16(val), r.value)
+    assert np.array_equal(kb[..., :dn], r.key[..., :dn])
+    check_bf16(kb, r.key, "kv key bf16 narrow")
