@@ -81,10 +81,11 @@ typedef short v2i16_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2, float x3, int E) {
   const float scale = __uint_as_float(E > -127 ? (uint32_t)(E + 127) << 23 : 0x00400000u);
   const float lim = __uint_as_float(((uint32_t)(E + 135) << 23) | 0x00600000u);  // 1.75 * 2^(E+8)
-  x0 = fminf(fmaxf(x0, -lim), lim);
-  x1 = fminf(fmaxf(x1, -lim), lim);
-  x2 = fminf(fmaxf(x2, -lim), lim);
-  x3 = fminf(fmaxf(x3, -lim), lim);
+  // one v_med3_f32 each (finite inputs: no NaN rule involved; -0 stays -0)
+  x0 = __builtin_amdgcn_fmed3f(x0, -lim, lim);
+  x1 = __builtin_amdgcn_fmed3f(x1, -lim, lim);
+  x2 = __builtin_amdgcn_fmed3f(x2, -lim, lim);
+  x3 = __builtin_amdgcn_fmed3f(x3, -lim, lim);
   v2i16_t o = {0, 0};
   o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, x0, x1, scale, false);
   o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, x2, x3, scale, true);
