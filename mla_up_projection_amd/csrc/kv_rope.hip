@@ -20,6 +20,7 @@ namespace {
 
 constexpr int KV_TOK = 8;         // tokens per workgroup chunk
 constexpr int KV_MAX_ROPE = 256;  // widest rope slice (the ABI limits d_rope to this)
+constexpr int KV_ROT_PITCH = KV_MAX_ROPE + 4;  // LDS row pitch: tokens' rows in different banks
 
 // A workgroup owns KV_TOK consecutive tokens, all heads. It first rotates
 // the tokens' shared k_pe slices once into LDS (with the tokens' BHSD
@@ -31,7 +32,7 @@ constexpr int KV_MAX_ROPE = 256;  // widest rope slice (the ABI limits d_rope to
 template <int EPT>
 __global__ __launch_bounds__(256) void kv_rope_kernel(KvParams p) {
   constexpr int NG = EPT / 8;
-  __shared__ float rot[KV_TOK * KV_MAX_ROPE];
+  __shared__ float rot[KV_TOK * KV_ROT_PITCH];
   __shared__ int64_t orow0[KV_TOK];  // BHSD row of head 0: (b H) S + s
   const int Dk = p.d_nope + p.d_rope;
   const int row_in = p.d_nope + p.d_v;
@@ -58,8 +59,8 @@ __global__ __launch_bounds__(256) void kv_rope_kernel(KvParams p) {
         const float nan = __builtin_nanf("");
         const int64_t ti = (int64_t)(ok ? pos : 0) * p.rope_pairs + k;
         const float c = ok ? p.cos[ti] : nan, sn = ok ? p.sin[ti] : nan;
-        rot[tl * KV_MAX_ROPE + 2 * k] = a * c - bb * sn;
-        rot[tl * KV_MAX_ROPE + 2 * k + 1] = a * sn + bb * c;
+        rot[tl * KV_ROT_PITCH + 2 * k] = a * c - bb * sn;
+        rot[tl * KV_ROT_PITCH + 2 * k + 1] = a * sn + bb * c;
       }
     }
     __syncthreads();
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(256) void kv_rope_kernel(KvParams p) {
         for (int q = 0; q < NG; ++q) {
           const int d = d0[w] + 8 * q;
           if (key[w] && d >= p.d_nope) {
-            const float* r = rot + tl[w] * KV_MAX_ROPE + (d - p.d_nope);
+            const float* r = rot + tl[w] * KV_ROT_PITCH + (d - p.d_nope);
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[8 * q + k] = r[k];
           } else {
