@@ -758,3 +758,16 @@ def test_kv_rope_bf16_widths_not_multiple_of_32():
     assert np.array_equal(bits16(val), r.value)
     assert np.array_equal(kb[..., :dn], r.key[..., :dn])
     check_bf16(kb, r.key, "kv key bf16 narrow")
+
+
+@pytest.mark.parametrize("fp8_mfma", [False, True])
+def test_bwd_mxfp8_split_reduction_small(fp8_mfma):
+    """One dX tile and eight 128-value stages: the reduction over n is split in
+    two (fp32 partials summed in order), on a shape the oracle does whole."""
+    T, K, H, dn, dr = 128, 192, 8, 64, 64
+    x = syn.normal_bf16((T, K), 1.0, 210)
+    w = syn.normal_bf16((H * (dn + dr), K), 0.05, 211)
+    dq = syn.normal_bf16((T, H, dn + dr), 1e-2, 212)
+    g = run_bwd(dq, x, w, H=H, dn=dn, dr=dr, S=T, mx=fp8_mfma, dw_fp32=True)
+    r = o.qup_backward_mxfp8(dq, x, w, H=H, d_nope=dn, d_rope=dr, cos=g["oc"], sin=g["os"], S=T)
+    _check_mx_bwd(g, r, f"mx bwd split fp8_mfma={fp8_mfma}", fp8_mfma)
