@@ -76,7 +76,7 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the operation runs on a single GPU; see the sharding notes in DESIGN.md)",
+              "(the operation runs on a single GPU; sharding it across GPUs is not implemented)",
               file=sys.stderr)
         sys.exit(2)
 
