@@ -771,3 +771,49 @@ def test_bwd_mxfp8_split_reduction_small(fp8_mfma):
     g = run_bwd(dq, x, w, H=H, dn=dn, dr=dr, S=T, mx=fp8_mfma, dw_fp32=True)
     r = o.qup_backward_mxfp8(dq, x, w, H=H, d_nope=dn, d_rope=dr, cos=g["oc"], sin=g["os"], S=T)
     _check_mx_bwd(g, r, f"mx bwd split fp8_mfma={fp8_mfma}", fp8_mfma)
+
+
+def test_bwd_and_kv_leave_inputs_untouched_and_repeat_bit_identically():
+    """The backward (bf16 and MXFP8) and the KV side write fresh outputs only:
+    every input is byte-identical afterwards, and a second run gives the same
+    bits (no floating-point atomics)."""
+    T, K, H, dn, dr, dv = 256, 128, 4, 64, 64, 64
+    x = _dev(syn.normal_bf16((T, K), 1.0, 220))
+    w = _dev(syn.normal_bf16((H * (dn + dr), K), 0.05, 221))
+    dq = _dev(syn.normal_bf16((T, H, dn + dr), 1e-2, 222))
+    kv = _dev(syn.normal_bf16((T, H, dn + dv), 1.0, 223))
+    pe = _dev(syn.normal_bf16((T, dr), 1.0, 224))
+    cos, sin, _, _ = rope_tables(T, dr)
+    before = [_hash(t) for t in (x, w, dq, kv, pe, cos, sin)]
+    N = H * (dn + dr)
+
+    def run():
+        outs = []
+        for mx in (None, False, True):
+            dq_pre = torch.empty(T, N, dtype=torch.bfloat16, device=DEV)
+            dx = torch.empty(T, K, dtype=torch.bfloat16, device=DEV)
+            dw = torch.empty(N, K, dtype=torch.float32, device=DEV)
+            db = torch.empty(N, dtype=torch.bfloat16, device=DEV)
+            kw = dict(H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin, dx=dx, dw=dw, db=db, use_bias=True,
+                      B=1, S=T)
+            if mx is None:
+                ws = torch.empty(max(m.mla_qup_bwd_workspace_size(dq, x, w, dq_pre, **kw), 1),
+                                 dtype=torch.uint8, device=DEV)
+                m.mla_qup_bwd(dq, x, w, dq_pre, workspace=ws, **kw)
+            else:
+                ws = torch.empty(m.mla_qup_bwd_mxfp8_workspace_size(dq, x, w, dq_pre, **kw), dtype=torch.uint8,
+                                 device=DEV)
+                m.mla_qup_bwd_mxfp8(dq, x, w, dq_pre, workspace=ws, fp8_mfma=mx, **kw)
+            outs += [dq_pre, dx, dw, db]
+        key = torch.empty(1, H, T, dn + dr, dtype=torch.uint8, device=DEV)
+        ks = torch.empty(1, H, T, (dn + dr) // 32, dtype=torch.uint8, device=DEV)
+        val = torch.empty(1, H, T, dv, dtype=torch.uint8, device=DEV)
+        vs = torch.empty(1, H, T, dv // 32, dtype=torch.uint8, device=DEV)
+        m.mla_kv_rope(kv, pe, key, val, H=H, d_nope=dn, d_rope=dr, d_v=dv, cos=cos, sin=sin, key_scales=ks,
+                      value_scales=vs, B=1, S=T)
+        torch.cuda.synchronize()
+        return [_hash(t) for t in outs + [key, ks, val, vs]]
+
+    first, second = run(), run()
+    assert first == second
+    assert [_hash(t) for t in (x, w, dq, kv, pe, cos, sin)] == before
