@@ -25,6 +25,7 @@ struct FwdParams {
   int rope_rows, rope_pairs;
   int out_mx;              // 1: MXFP8 codes + scales, 0: bf16
   int mx_fp8_mfma;         // MXFP8 operands on the scaled FP8 MFMA (else exact bf16 MFMA)
+  int rope_lds;            // set by the launcher: stage each tile's table rows in LDS
   // plain product form (launch_mx_gemm): out[t][n] row-major with stride N,
   // fp32 when out_f32 (else bf16); K split into k_splits stage ranges, range
   // s writing at out + s * split_stride bytes

@@ -47,6 +47,13 @@ constexpr int WAVES_N = TILE_N / (32 * WBLK_N);  // waves along N (2); along T: 
 static_assert(WAVES_N * (TILE_T / (32 * WBLK_T)) == NTHREADS / 64, "2 x 2 waves");
 static_assert(WBLK_N == 3, "packed scale stores below are written for 3 blocks per wave");
 constexpr int WG_PER_CU = 2;              // two independent workgroups per CU
+constexpr int ROPE_ROW_BYTES = 128;       // LDS-staged table rows: 32 fp32 pairs (d_rope = 64)
+constexpr int ROPE_TAB_HALF = TILE_T * ROPE_ROW_BYTES;  // cos rows, then sin rows (32 KB in all)
+
+// LDS-staged table rows: 16-byte chunk c of token row r sits at chunk
+// position c ^ rope_swz(r), so the 32 rows one half-wave reads in the
+// epilogue spread over the banks.
+__device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 
 enum { MODE_BF16 = 0, MODE_MX_EXACT = 1, MODE_MX_FP8 = 2, MODE_BF16_R64 = 3 };
 enum { EPI_MLA = 0, EPI_PLAIN = 1 };  // fused RoPE/quantize/BHSD epilogue, or a plain row-major store
@@ -105,9 +112,12 @@ __device__ __forceinline__ TokInfo tok_info(const FwdParams& p, const TokenMap& 
 
 // One 32 (n) x 32 (token) block: bias, rotation, quantization, store.
 // Returns the block's E8M0 scale byte (MXFP8 output), which the caller
-// stores; `store_scale` makes this function store it itself instead.
+// stores; `store_scale` makes this function store it itself instead. `tab`
+// is the tile's cos/sin rows staged in LDS (see stage_rope_rows) or null, and
+// `tok` this lane's token row inside the tile.
 __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const TokInfo& ti, const f32x16_t& acc,
-                                                   int n_blk, int lane, bool store_scale) {
+                                                   int n_blk, int lane, bool store_scale, const uint8_t* tab,
+                                                   int tok) {
   const int half = lane >> 5;
   const int h = n_blk / p.D;
   const int d_blk = n_blk - h * p.D;
@@ -138,10 +148,22 @@ __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const Tok
       // 8-byte sin load, all eight issued before any use.
       const int i0 = ((d_blk - p.d_nope) >> 1) + 2 * half;
       float2 cc[4], ss[4];
+      if (tab) {
+        // pair i0 + 4g is chunk i0 / 4 + g, bytes 8 half .. +7 of it
+        const uint8_t* row = tab + tok * ROPE_ROW_BYTES + 8 * half;
+        const int sw = rope_swz(tok);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        cc[g] = *reinterpret_cast<const float2*>(p.cos + trow + i0 + 4 * g);
-        ss[g] = *reinterpret_cast<const float2*>(p.sin + trow + i0 + 4 * g);
+        for (int g = 0; g < 4; ++g) {
+          const int c = ((i0 >> 2) + g) ^ sw;
+          cc[g] = *reinterpret_cast<const float2*>(row + 16 * c);
+          ss[g] = *reinterpret_cast<const float2*>(row + ROPE_TAB_HALF + 16 * c);
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          cc[g] = *reinterpret_cast<const float2*>(p.cos + trow + i0 + 4 * g);
+          ss[g] = *reinterpret_cast<const float2*>(p.sin + trow + i0 + 4 * g);
+        }
       }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -225,25 +247,26 @@ __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const Tok
 template <int TB, int NB>
 __device__ __forceinline__ void epilogue_one(const FwdParams& p, const TokInfo& ti,
                                              const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int lane,
-                                             bool packed, uint32_t (&sc)[WBLK_N]) {
+                                             bool packed, uint32_t (&sc)[WBLK_N], const uint8_t* tab, int tok) {
   const int n_blk = n0 + 32 * NB;
   // one block at a time: interleaving blocks would hold several blocks'
   // temporaries live next to the accumulators
   __builtin_amdgcn_sched_barrier(0);
-  sc[NB] = n_blk < p.N ? epilogue_block(p, ti, acc[NB][TB], n_blk, lane, !packed) : 0u;
+  sc[NB] = n_blk < p.N ? epilogue_block(p, ti, acc[NB][TB], n_blk, lane, !packed, tab, tok) : 0u;
 }
 
 template <int TB, int... NBs>
 __device__ __forceinline__ void epilogue_tok(const FwdParams& p, const TokenMap& tm,
                                              const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int64_t t_lane,
-                                             int lane, std::integer_sequence<int, NBs...>) {
+                                             int lane, const uint8_t* tab, int tok0,
+                                             std::integer_sequence<int, NBs...>) {
   const TokInfo ti = tok_info(p, tm, t_lane + 32 * TB);
   // When the tile is exactly one head, the head's D/32 scale bytes of this
   // token are contiguous: store them as 16-bit pairs, right after the token
   // row's codes, instead of one byte per block.
   const bool packed = p.out_mx && p.D == TILE_N;
   uint32_t sc[WBLK_N];
-  (epilogue_one<TB, NBs>(p, ti, acc, n0, lane, packed, sc), ...);
+  (epilogue_one<TB, NBs>(p, ti, acc, n0, lane, packed, sc, tab, tok0 + 32 * TB), ...);
   if (packed && ti.ok && lane < 32) {
     // this wave's 3 scale bytes of the token's head: one 16-bit and one byte store
     const int64_t row = ti.row + (int64_t)(n0 / p.D) * p.S;
@@ -261,14 +284,39 @@ __device__ __forceinline__ void epilogue_tok(const FwdParams& p, const TokenMap&
 template <int... TBs>
 __device__ __forceinline__ void epilogue_all(const FwdParams& p, const TokenMap& tm,
                                              const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int64_t t_lane,
-                                             int lane, std::integer_sequence<int, TBs...>) {
-  (epilogue_tok<TBs>(p, tm, acc, n0, t_lane, lane, std::make_integer_sequence<int, WBLK_N>{}), ...);
+                                             int lane, const uint8_t* tab, int tok0,
+                                             std::integer_sequence<int, TBs...>) {
+  (epilogue_tok<TBs>(p, tm, acc, n0, t_lane, lane, tab, tok0, std::make_integer_sequence<int, WBLK_N>{}), ...);
 }
 
+// t_lane: this lane's first token; tok0: its row inside the tile (for tab).
 __device__ __forceinline__ void epilogue_tile(const FwdParams& p, const TokenMap& tm,
                                               const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int64_t t_lane,
-                                              int lane) {
-  epilogue_all(p, tm, acc, n0, t_lane, lane, std::make_integer_sequence<int, WBLK_T>{});
+                                              int lane, const uint8_t* tab, int tok0) {
+  epilogue_all(p, tm, acc, n0, t_lane, lane, tab, tok0, std::make_integer_sequence<int, WBLK_T>{});
+}
+
+// The tile's cos and sin table rows (d_rope = 64: the first 32 pairs of
+// each row, 128 bytes) DMA'd into a free ring slot: [cos rows of the 128
+// tokens][sin rows], row r at r * 128. Wave load j = 4q + wave fills rows
+// 8j .. 8j + 7 of both tables; lane i writes row 8j + i / 8, chunk position
+// i % 8. Positions outside the table (and rows past T) read row 0; the
+// epilogue turns those tokens into NaN as it does for direct table loads.
+__device__ __forceinline__ void stage_rope_rows(const FwdParams& p, const TokenMap& tm, int64_t t0,
+                                                uint32_t dst, int wave, int lane) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = 4 * q + wave;
+    const int r = 8 * j + (lane >> 3);
+    int64_t t = t0 + r;
+    if (t >= p.T) t = p.T - 1;
+    int pos, b, s;
+    token_coords(tm, t, pos, b, s);
+    if (pos < 0 || pos >= p.rope_rows) pos = 0;
+    const uint32_t off = (uint32_t)pos * (uint32_t)(p.rope_pairs * 4) + (uint32_t)(((lane & 7) ^ rope_swz(r)) * 16);
+    dma16(p.cos, off, dst + j * 1024);
+    dma16(p.sin, off, dst + ROPE_TAB_HALF + j * 1024);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -596,6 +644,7 @@ void qup_fwd_kernel(FwdParams p) {
   constexpr int STAGES = TL::STAGES;
   constexpr int RING = TL::SB * STAGES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[RING];
+  static_assert(STAGES != 2 || 2 * ROPE_TAB_HALF <= TL::SB, "table rows must fit one slot");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -626,8 +675,17 @@ void qup_fwd_kernel(FwdParams p) {
   ScaleRows sr{};
   StageScales sc_next{}, sc_cur{};
   if (MX) sr = scale_rows(p, t0, n0, arow0, brow0, un_.kt0);
+  // stage s of the current tile lives in slot (sb + s) % STAGES; each tile
+  // starts where the previous one's stage sequence (nk + STAGES - 1 issued
+  // stages) left off
+  int sb = 0;
+  // With two slots, the last iteration's spare load (past the last stage)
+  // brings the tile's cos/sin rows instead, so they land during the last
+  // stage's MFMAs rather than after the loop (measured: FP8 MFMA mode 4.6 %
+  // faster, BF16 0.5 %; the exact MXFP8 mode 1 % slower, so not there).
+  const bool tab_lds = STAGES == 2 && MODE != MODE_MX_EXACT && EPI != EPI_PLAIN && p.rope_lds;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, s, ring, wave);
+  for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, sb + s, ring, wave);
   if (MX) sc_next = load_scales(p, sr, 0, nk);  // MX: STAGES == 2, one stage ahead
 
   for (;;) {
@@ -646,14 +704,17 @@ void qup_fwd_kernel(FwdParams p) {
       // iteration has the same number of loads in flight; slot
       // (kt + STAGES - 1) % STAGES was read in iteration kt - 1 and every
       // wave has passed the barrier since.
-      issue_stage<MODE>(dp, xb, wb, kt + STAGES - 1, nk, kt + STAGES - 1, ring, wave);
+      if (tab_lds && kt == nk - 1)
+        stage_rope_rows(p, tm, t0, ring + (uint32_t)((sb + nk) % STAGES) * TL::SB, wave, lane);
+      else
+        issue_stage<MODE>(dp, xb, wb, kt + STAGES - 1, nk, sb + kt + STAGES - 1, ring, wave);
       if (MX) {
         // stage kt's scales arrived with its DMA (the wait above covers all
         // vector loads); stage kt + 1's go out with its DMA
         sc_cur = sc_next;
         sc_next = load_scales(p, sr, kt + 1, nk);
       }
-      mma_stage<MODE>(acc, lds + (kt % STAGES) * TL::SB, sc_cur, arow0, brow0, half);
+      mma_stage<MODE>(acc, lds + ((sb + kt) % STAGES) * TL::SB, sc_cur, arow0, brow0, half);
     }
 
     // Next tile of this workgroup: start its first stages before the
@@ -663,6 +724,8 @@ void qup_fwd_kernel(FwdParams p) {
     const int64_t t0c = t0;
     const int n0c = n0;
     const int split_c = un_.split;
+    const uint8_t* tab = tab_lds ? lds + ((sb + nk) % STAGES) * TL::SB : nullptr;
+    sb = (sb + nk + STAGES - 1) % STAGES;  // the next tile's stage 0 avoids the table's slot
     vm_wait<0>();
     barrier();
     if (more) {
@@ -674,7 +737,7 @@ void qup_fwd_kernel(FwdParams p) {
       wb = static_cast<const uint8_t*>(p.w) + (int64_t)un_.kt0 * TL::ROWB;
       dp = dma_plan<MODE>(p, t0, n0, wave, lane, row_bytes);
 #pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, s, ring, wave);
+      for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, sb + s, ring, wave);
       if (MX) {
         sr = scale_rows(p, t0, n0, arow0, brow0, un_.kt0);
         sc_next = load_scales(p, sr, 0, nk);
@@ -684,7 +747,8 @@ void qup_fwd_kernel(FwdParams p) {
       plain_tile(p, static_cast<uint8_t*>(p.out) + (int64_t)split_c * p.split_stride, acc,
                  n0c + 32 * WBLK_N * wn, t0c + 32 * WBLK_T * wt + (lane & 31), lane);
     else
-      epilogue_tile(p, tm, acc, n0c + 32 * WBLK_N * wn, t0c + 32 * WBLK_T * wt + (lane & 31), lane);
+      epilogue_tile(p, tm, acc, n0c + 32 * WBLK_N * wn, t0c + 32 * WBLK_T * wt + (lane & 31), lane, tab,
+                    32 * WBLK_T * wt + (lane & 31));
     if (!more) break;
     u = un;
   }
@@ -701,7 +765,20 @@ int fwd_grid(const FwdParams& p, int num_cus) {
 }
 
 
-hipError_t launch_qup_fwd_bf16(const FwdParams& p, hipStream_t stream) {
+namespace {
+// Table rows can be staged in LDS when the rope slice is 64 wide (the first
+// 32 pairs of a row, 128 bytes), rows start 16-byte aligned and every row
+// offset fits the 32-bit DMA offset.
+bool rope_rows_fit_lds(const FwdParams& p) {
+  const auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  return p.d_rope == 64 && p.rope_pairs % 4 == 0 && p.rope_rows > 0 && a16(p.cos) && a16(p.sin) &&
+         (int64_t)p.rope_rows * p.rope_pairs * 4 <= (int64_t)UINT32_MAX;
+}
+}  // namespace
+
+hipError_t launch_qup_fwd_bf16(const FwdParams& p_in, hipStream_t stream) {
+  FwdParams p = p_in;
+  p.rope_lds = rope_rows_fit_lds(p);
   const dim3 grid(fwd_grid(p, device_cu_count()));
   if (p.K % 64 == 0)
     hipLaunchKernelGGL((qup_fwd_kernel<MODE_BF16, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
@@ -710,7 +787,9 @@ hipError_t launch_qup_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_qup_fwd_mx(const FwdParams& p, hipStream_t stream) {
+hipError_t launch_qup_fwd_mx(const FwdParams& p_in, hipStream_t stream) {
+  FwdParams p = p_in;
+  p.rope_lds = rope_rows_fit_lds(p);
   const dim3 grid(fwd_grid(p, device_cu_count()));
   if (p.mx_fp8_mfma)
     hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_FP8, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
