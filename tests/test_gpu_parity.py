@@ -307,6 +307,28 @@ def test_fwd_position_beyond_table_is_nan_not_a_read():
     assert (s[:, pos >= 32] == 0xFF).all() and (s[:, pos < 32] != 0xFF).all()
 
 
+def test_fwd_position_beyond_table_is_nan_with_a_64_wide_rope_slice():
+    """The same with heads of 128 + 64 (the table rows of a tile are staged
+    in LDS on this path): rows past the table give NaN rope blocks only."""
+    lengths = [40, 30]
+    cu = _dev(syn.cu_seqlens_of(lengths))
+    T, K, H, dn, dr = 70, 64, 1, 128, 64
+    x = _dev(syn.normal_bf16((T, K), 1.0, 52))
+    w = _dev(syn.normal_bf16((H * (dn + dr), K), 0.1, 53))
+    cos = torch.empty(32, dr // 2, device=DEV)
+    sin = torch.empty_like(cos)
+    m.rope_cache_build(cos, sin, dr, 1e4)
+    out = torch.empty(1, H, T, dn + dr, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(1, H, T, (dn + dr) // 32, dtype=torch.uint8, device=DEV)
+    m.mla_qup_fwd(x, w, out, H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin, out_scales=sc,
+                  fmt=m.FMT_THD, cu_seqlens=cu, max_seqlen=32)
+    torch.cuda.synchronize()
+    s = sc.cpu()[0, 0]                       # [T, 6]: blocks 0..3 nope, 4..5 rope
+    pos = np.array(list(range(40)) + list(range(30)))
+    assert (s[pos >= 32][:, 4:] == 0xFF).all() and (s[pos < 32][:, 4:] != 0xFF).all()
+    assert (s[:, :4] != 0xFF).all()
+
+
 # ------------------------------------------------------------ backward ------
 def run_bwd(dq, x, w, *, H, dn, dr, fmt=m.FMT_BSHD, B=1, S=None, cu=None, max_seqlen=None,
             use_bias=True, dw_fp32=False, yarn=None, mx=None, want=("dx", "dw")):
