@@ -839,3 +839,41 @@ def test_bwd_and_kv_leave_inputs_untouched_and_repeat_bit_identically():
     first, second = run(), run()
     assert first == second
     assert [_hash(t) for t in (x, w, dq, kv, pe, cos, sin)] == before
+
+
+@pytest.mark.parametrize("dn,dr,H", [(128, 64, 2), (32, 32, 3)])
+def test_fwd_epilogue_bit_exact_on_exactly_representable_values(dn, dr, H):
+    """Inputs whose every pre-quantization value is exact in float32 in any
+    summation order: small-integer X and W (each W row scaled by its own power
+    of two, so blocks get different exponents), an integer bias, and a cos/sin
+    table of quarter turns only (c, s in {0, +-1}), passed in by the caller.
+    The GPU's float32 values then equal the oracle's, so the fused epilogue's
+    rotation, E8M0 scales, E4M3 codes and bf16 rounding must match the oracle
+    bit for bit, with no accumulation-order allowance. dr = 64 takes the path
+    that stages the table rows in LDS; 32 reads the table directly."""
+    T, K = 200, 128
+    D = dn + dr
+    N = H * D
+    rng = np.random.default_rng(230 + dr)
+    xf = rng.integers(-3, 4, (T, K)).astype(np.float32)
+    wf = (rng.integers(-3, 4, (N, K)) * np.exp2(rng.integers(-4, 5, (N, 1)))).astype(np.float32)
+    bf = (rng.integers(-40, 41, (N,)) * 0.25).astype(np.float32)
+    x, w, bias = (torch.from_numpy(a).to(torch.bfloat16) for a in (xf, wf, bf))
+    quarter = rng.integers(0, 4, (T, dr // 2))
+    oc = np.choose(quarter, [1.0, 0.0, -1.0, 0.0]).astype(np.float32)
+    os_ = np.choose(quarter, [0.0, 1.0, 0.0, -1.0]).astype(np.float32)
+    cos, sin = torch.from_numpy(oc).to(DEV), torch.from_numpy(os_).to(DEV)
+    for out_dtype in ("mxfp8", "bf16"):
+        mx = out_dtype == "mxfp8"
+        out = torch.empty(1, H, T, D, dtype=torch.uint8 if mx else torch.bfloat16, device=DEV)
+        sc = torch.empty(1, H, T, D // 32, dtype=torch.uint8, device=DEV) if mx else None
+        m.mla_qup_fwd(_dev(x), _dev(w), out, H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin, bias=_dev(bias),
+                      out_scales=sc, B=1, S=T)
+        torch.cuda.synchronize()
+        r = o.qup_forward(x, w, H=H, d_nope=dn, d_rope=dr, cos=oc, sin=os_, B=1, S=T, bias=bias,
+                          out_dtype=out_dtype)
+        if mx:
+            assert np.array_equal(sc.cpu().numpy(), r.scales)
+            assert np.array_equal(out.cpu().numpy(), r.out)
+        else:
+            assert np.array_equal(bits16(out), r.out)
