@@ -417,8 +417,9 @@ __device__ __forceinline__ void frag_mx_exact(const uint8_t* rowp, int c, int r,
 
 // MXFP8 operand scales of one stage for this lane's fragment rows: the four
 // E8M0 bytes of K blocks 4k .. 4k+3 of W rows arow0 + 32 nb and of X rows
-// brow0 + 32 tb, one aligned dword per row (K % 128 == 0), loaded with the
-// stage's DMA and consumed after the same wait.
+// brow0 + 32 tb (one dword per row and stage, K % 128 == 0). In the FP8 MFMA
+// mode only the two bytes this lane passes are kept, in bytes 0 and 1 (see
+// mma_stage).
 struct StageScales {
   uint32_t w[WBLK_N];
   uint32_t x[WBLK_T];
@@ -448,13 +449,61 @@ __device__ __forceinline__ ScaleRows scale_rows(const FwdParams& p, int64_t t0, 
   return sr;
 }
 
-__device__ __forceinline__ StageScales load_scales(const FwdParams& p, const ScaleRows& sr, int kt, int nk) {
-  const int k4 = 4 * (kt < nk ? kt : nk - 1);
+// Scales travel in pairs of stages: for pair j, the lane in wave half h
+// loads the dword of stage 2j + h of each of its rows (the two halves hold
+// the same rows), and one half-swap gives every lane both stages' dwords.
+// That is half the load instructions and cache-line visits of one dword per
+// lane and stage, in the same registers.
+__device__ __forceinline__ StageScales load_pair(const FwdParams& p, const ScaleRows& sr, int j, int nk,
+                                                 int half) {
+  int kt = 2 * j + half;
+  if (kt > nk - 1) kt = nk - 1;
+  const int k4 = 4 * kt;
   StageScales sc;
 #pragma unroll
   for (int nb = 0; nb < WBLK_N; ++nb) sc.w[nb] = *reinterpret_cast<const uint32_t*>(p.ws + sr.w[nb] + k4);
 #pragma unroll
   for (int tb = 0; tb < WBLK_T; ++tb) sc.x[tb] = *reinterpret_cast<const uint32_t*>(p.xs + sr.x[tb] + k4);
+  return sc;
+}
+
+// The pair's dwords in use: s[0] for the even stage, s[1] for the odd one.
+// FP8 MFMA mode packs the bytes the lane passes (blocks h and 2 + h of each
+// stage, h the wave half) into s[0]: even stage in bytes 0-1, odd in 2-3.
+struct PairScales {
+  StageScales s[2];
+};
+
+template <bool FP8>
+__device__ __forceinline__ PairScales unpack_pair(const StageScales& raw, int half) {
+  PairScales ps;
+  const uint32_t sel = half ? 0x07050301u : 0x06040200u;
+  const auto one = [&](uint32_t v, uint32_t& e, uint32_t& o) {
+    const u32x2_t t = swap_halves(v, v);  // {stage 2j, stage 2j + 1} in every lane
+    if (FP8) {
+      e = __builtin_amdgcn_perm(t[1], t[0], sel);
+      o = 0;
+    } else {
+      e = t[0];
+      o = t[1];
+    }
+  };
+#pragma unroll
+  for (int nb = 0; nb < WBLK_N; ++nb) one(raw.w[nb], ps.s[0].w[nb], ps.s[1].w[nb]);
+#pragma unroll
+  for (int tb = 0; tb < WBLK_T; ++tb) one(raw.x[tb], ps.s[0].x[tb], ps.s[1].x[tb]);
+  return ps;
+}
+
+// Scales of stage kt of the current pair.
+template <bool FP8>
+__device__ __forceinline__ StageScales stage_scales(const PairScales& ps, int kt) {
+  const bool odd = kt & 1;
+  StageScales sc;
+#pragma unroll
+  for (int nb = 0; nb < WBLK_N; ++nb) sc.w[nb] = FP8 ? ps.s[0].w[nb] >> (odd ? 16 : 0) : (odd ? ps.s[1].w[nb] : ps.s[0].w[nb]);
+#pragma unroll
+  for (int tb = 0; tb < WBLK_T; ++tb) sc.x[tb] = FP8 ? ps.s[0].x[tb] >> (odd ? 16 : 0) : (odd ? ps.s[1].x[tb] : ps.s[0].x[tb]);
   return sc;
 }
 
@@ -527,7 +576,7 @@ __device__ __forceinline__ void mma_stage(f32x16_t (&acc)[WBLK_N][WBLK_T], const
     for (int st = 0; st < TL::KPS / 64; ++st) {
       i32x8_t a[WBLK_N], b[WBLK_T];
       uint32_t sa[WBLK_N], sb[WBLK_T];
-      const int sh = 8 * (2 * st + half);
+      const int sh = 8 * st;  // packed: this lane's block 2 st + half
 #pragma unroll
       for (int nb = 0; nb < WBLK_N; ++nb) {
         const int r = arow0 + 32 * nb;
@@ -673,7 +722,8 @@ void qup_fwd_kernel(FwdParams p) {
   const uint8_t* wb = static_cast<const uint8_t*>(p.w) + (int64_t)un_.kt0 * TL::ROWB;
   DmaPlan<MODE> dp = dma_plan<MODE>(p, t0, n0, wave, lane, row_bytes);
   ScaleRows sr{};
-  StageScales sc_next{}, sc_cur{};
+  StageScales sc_raw{}, sc_cur{};
+  PairScales sc_pair{};
   if (MX) sr = scale_rows(p, t0, n0, arow0, brow0, un_.kt0);
   // stage s of the current tile lives in slot (sb + s) % STAGES; each tile
   // starts where the previous one's stage sequence (nk + STAGES - 1 issued
@@ -686,7 +736,7 @@ void qup_fwd_kernel(FwdParams p) {
   const bool tab_lds = STAGES == 2 && MODE != MODE_MX_EXACT && EPI != EPI_PLAIN && p.rope_lds;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, sb + s, ring, wave);
-  if (MX) sc_next = load_scales(p, sr, 0, nk);  // MX: STAGES == 2, one stage ahead
+  if (MX) sc_raw = load_pair(p, sr, 0, nk, half);  // MX: STAGES == 2
 
   for (;;) {
     f32x16_t acc[WBLK_N][WBLK_T];
@@ -709,10 +759,13 @@ void qup_fwd_kernel(FwdParams p) {
       else
         issue_stage<MODE>(dp, xb, wb, kt + STAGES - 1, nk, sb + kt + STAGES - 1, ring, wave);
       if (MX) {
-        // stage kt's scales arrived with its DMA (the wait above covers all
-        // vector loads); stage kt + 1's go out with its DMA
-        sc_cur = sc_next;
-        sc_next = load_scales(p, sr, kt + 1, nk);
+        // pair kt / 2 arrived (the wait above covers all vector loads); the
+        // next pair goes out with stage kt + 1's DMA
+        if ((kt & 1) == 0) {
+          sc_pair = unpack_pair<MODE == MODE_MX_FP8>(sc_raw, half);
+          sc_raw = load_pair(p, sr, kt / 2 + 1, nk, half);
+        }
+        sc_cur = stage_scales<MODE == MODE_MX_FP8>(sc_pair, kt);
       }
       mma_stage<MODE>(acc, lds + ((sb + kt) % STAGES) * TL::SB, sc_cur, arow0, brow0, half);
     }
@@ -740,7 +793,7 @@ void qup_fwd_kernel(FwdParams p) {
       for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, sb + s, ring, wave);
       if (MX) {
         sr = scale_rows(p, t0, n0, arow0, brow0, un_.kt0);
-        sc_next = load_scales(p, sr, 0, nk);
+        sc_raw = load_pair(p, sr, 0, nk, half);
       }
     }
     if (EPI == EPI_PLAIN)
