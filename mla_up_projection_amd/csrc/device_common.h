@@ -123,6 +123,13 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
 }
 
+// 8-byte LDS read at an LDS byte address (ds_read_b64; 8-byte aligned).
+__device__ __forceinline__ float2 lds_read_f2(uint32_t addr) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = *reinterpret_cast<__attribute__((address_space(3))) const f32x2_t*>((uintptr_t)addr);
+  return make_float2(v[0], v[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Token row -> (position, b, s). See the token-format comment in mla_qup.h.
 // ---------------------------------------------------------------------------

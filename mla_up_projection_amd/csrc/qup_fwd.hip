@@ -94,6 +94,13 @@ __device__ __forceinline__ int roff(int r, int c) { return r * ROWB + ((c ^ swz<
 // Fused epilogue for one 32 (n) x 32 (token) accumulator block.
 // acc[r] holds row 8*(r/4) + 4*(lane/32) + r%4 of the block, token lane%32.
 // ---------------------------------------------------------------------------
+// The tile's cos/sin rows staged in LDS (see stage_rope_rows): `on` is
+// wave-uniform, `addr` the LDS byte address of the cos rows.
+struct RopeTab {
+  bool on;
+  uint32_t addr;
+};
+
 struct TokInfo {
   bool ok;      // token row < T
   int pos;      // RoPE position
@@ -110,13 +117,20 @@ __device__ __forceinline__ TokInfo tok_info(const FwdParams& p, const TokenMap& 
   return ti;
 }
 
+// Rotation of the pair (a, b) by the angle with cosine c and sine s, as
+// (a c - b s, a s + b c): each output is one rounded product and one fused
+// multiply-add, written out so the rounding does not depend on how the
+// compiler contracts the surrounding code.
+__device__ __forceinline__ float rot_lo(float a, float b, float c, float s) { return __builtin_fmaf(a, c, -(b * s)); }
+__device__ __forceinline__ float rot_hi(float a, float b, float c, float s) { return __builtin_fmaf(a, s, b * c); }
+
 // One 32 (n) x 32 (token) block: bias, rotation, quantization, store.
 // Returns the block's E8M0 scale byte (MXFP8 output), which the caller
 // stores; `store_scale` makes this function store it itself instead. `tab`
 // is the tile's cos/sin rows staged in LDS (see stage_rope_rows) or null, and
 // `tok` this lane's token row inside the tile.
 __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const TokInfo& ti, const f32x16_t& acc,
-                                                   int n_blk, int lane, bool store_scale, const uint8_t* tab,
+                                                   int n_blk, int lane, bool store_scale, RopeTab tab,
                                                    int tok) {
   const int half = lane >> 5;
   const int h = n_blk / p.D;
@@ -148,15 +162,17 @@ __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const Tok
       // 8-byte sin load, all eight issued before any use.
       const int i0 = ((d_blk - p.d_nope) >> 1) + 2 * half;
       float2 cc[4], ss[4];
-      if (tab) {
-        // pair i0 + 4g is chunk i0 / 4 + g, bytes 8 half .. +7 of it
-        const uint8_t* row = tab + tok * ROPE_ROW_BYTES + 8 * half;
+      if (tab.on) {
+        // pair i0 + 4g is chunk i0 / 4 + g, bytes 8 half .. +7 of it; LDS
+        // reads (ds_read_b64) by address, so they neither count against nor
+        // wait for the vector-memory loads in flight (the next tile's DMA)
+        const uint32_t row = tab.addr + (uint32_t)(tok * ROPE_ROW_BYTES + 8 * half);
         const int sw = rope_swz(tok);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int c = ((i0 >> 2) + g) ^ sw;
-          cc[g] = *reinterpret_cast<const float2*>(row + 16 * c);
-          ss[g] = *reinterpret_cast<const float2*>(row + ROPE_TAB_HALF + 16 * c);
+          const uint32_t c = (uint32_t)(((i0 >> 2) + g) ^ sw);
+          cc[g] = lds_read_f2(row + 16 * c);
+          ss[g] = lds_read_f2(row + ROPE_TAB_HALF + 16 * c);
         }
       } else {
 #pragma unroll
@@ -170,10 +186,10 @@ __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const Tok
         const float c0 = pos_ok ? cc[g].x : nan, c1 = pos_ok ? cc[g].y : nan;
         const float s0 = pos_ok ? ss[g].x : nan, s1 = pos_ok ? ss[g].y : nan;
         const float a0 = v[4 * g], b0 = v[4 * g + 1], a1 = v[4 * g + 2], b1 = v[4 * g + 3];
-        v[4 * g] = a0 * c0 - b0 * s0;
-        v[4 * g + 1] = a0 * s0 + b0 * c0;
-        v[4 * g + 2] = a1 * c1 - b1 * s1;
-        v[4 * g + 3] = a1 * s1 + b1 * c1;
+        v[4 * g] = rot_lo(a0, b0, c0, s0);
+        v[4 * g + 1] = rot_hi(a0, b0, c0, s0);
+        v[4 * g + 2] = rot_lo(a1, b1, c1, s1);
+        v[4 * g + 3] = rot_hi(a1, b1, c1, s1);
       }
     } else {
       // block straddling the nope/rope boundary, or unaligned table rows
@@ -185,10 +201,10 @@ __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const Tok
           const float c0 = pos_ok ? p.cos[trow + i] : nan, c1 = pos_ok ? p.cos[trow + i + 1] : nan;
           const float s0 = pos_ok ? p.sin[trow + i] : nan, s1 = pos_ok ? p.sin[trow + i + 1] : nan;
           const float a0 = v[4 * g], b0 = v[4 * g + 1], a1 = v[4 * g + 2], b1 = v[4 * g + 3];
-          v[4 * g] = a0 * c0 - b0 * s0;
-          v[4 * g + 1] = a0 * s0 + b0 * c0;
-          v[4 * g + 2] = a1 * c1 - b1 * s1;
-          v[4 * g + 3] = a1 * s1 + b1 * c1;
+          v[4 * g] = rot_lo(a0, b0, c0, s0);
+          v[4 * g + 1] = rot_hi(a0, b0, c0, s0);
+          v[4 * g + 2] = rot_lo(a1, b1, c1, s1);
+          v[4 * g + 3] = rot_hi(a1, b1, c1, s1);
         }
       }
     }
@@ -247,7 +263,7 @@ __device__ __forceinline__ uint32_t epilogue_block(const FwdParams& p, const Tok
 template <int TB, int NB>
 __device__ __forceinline__ void epilogue_one(const FwdParams& p, const TokInfo& ti,
                                              const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int lane,
-                                             bool packed, uint32_t (&sc)[WBLK_N], const uint8_t* tab, int tok) {
+                                             bool packed, uint32_t (&sc)[WBLK_N], RopeTab tab, int tok) {
   const int n_blk = n0 + 32 * NB;
   // one block at a time: interleaving blocks would hold several blocks'
   // temporaries live next to the accumulators
@@ -258,7 +274,7 @@ __device__ __forceinline__ void epilogue_one(const FwdParams& p, const TokInfo& 
 template <int TB, int... NBs>
 __device__ __forceinline__ void epilogue_tok(const FwdParams& p, const TokenMap& tm,
                                              const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int64_t t_lane,
-                                             int lane, const uint8_t* tab, int tok0,
+                                             int lane, RopeTab tab, int tok0,
                                              std::integer_sequence<int, NBs...>) {
   const TokInfo ti = tok_info(p, tm, t_lane + 32 * TB);
   // When the tile is exactly one head, the head's D/32 scale bytes of this
@@ -284,7 +300,7 @@ __device__ __forceinline__ void epilogue_tok(const FwdParams& p, const TokenMap&
 template <int... TBs>
 __device__ __forceinline__ void epilogue_all(const FwdParams& p, const TokenMap& tm,
                                              const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int64_t t_lane,
-                                             int lane, const uint8_t* tab, int tok0,
+                                             int lane, RopeTab tab, int tok0,
                                              std::integer_sequence<int, TBs...>) {
   (epilogue_tok<TBs>(p, tm, acc, n0, t_lane, lane, tab, tok0, std::make_integer_sequence<int, WBLK_N>{}), ...);
 }
@@ -292,7 +308,7 @@ __device__ __forceinline__ void epilogue_all(const FwdParams& p, const TokenMap&
 // t_lane: this lane's first token; tok0: its row inside the tile (for tab).
 __device__ __forceinline__ void epilogue_tile(const FwdParams& p, const TokenMap& tm,
                                               const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int64_t t_lane,
-                                              int lane, const uint8_t* tab, int tok0) {
+                                              int lane, RopeTab tab, int tok0) {
   epilogue_all(p, tm, acc, n0, t_lane, lane, tab, tok0, std::make_integer_sequence<int, WBLK_T>{});
 }
 
@@ -684,7 +700,10 @@ __device__ __forceinline__ Unit unit_coords(const TileGrid& g, const FwdParams& 
   return w;
 }
 
-template <int MODE, int EPI>
+// TAB: the tile's cos/sin rows are staged in LDS for the epilogue (a
+// compile-time choice, so that instantiation has no global table loads whose
+// waits would also wait for the next tile's DMA in flight).
+template <int MODE, int EPI, bool TAB = false>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(WG_PER_CU, WG_PER_CU)))
 void qup_fwd_kernel(FwdParams p) {
   using TL = Tile<MODE>;
@@ -731,9 +750,10 @@ void qup_fwd_kernel(FwdParams p) {
   int sb = 0;
   // With two slots, the last iteration's spare load (past the last stage)
   // brings the tile's cos/sin rows instead, so they land during the last
-  // stage's MFMAs rather than after the loop (measured: FP8 MFMA mode 4.6 %
-  // faster, BF16 0.5 %; the exact MXFP8 mode 1 % slower, so not there).
-  const bool tab_lds = STAGES == 2 && MODE != MODE_MX_EXACT && EPI != EPI_PLAIN && p.rope_lds;
+  // stage's MFMAs rather than after the loop, and the epilogue reads them
+  // with LDS reads that never wait for the next tile's DMA.
+  constexpr bool tab_lds = TAB;
+  static_assert(!TAB || (STAGES == 2 && EPI == EPI_MLA), "table staging uses the spare slot of a 2-slot ring");
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, sb + s, ring, wave);
   if (MX) sc_raw = load_pair(p, sr, 0, nk, half);  // MX: STAGES == 2
@@ -777,7 +797,7 @@ void qup_fwd_kernel(FwdParams p) {
     const int64_t t0c = t0;
     const int n0c = n0;
     const int split_c = un_.split;
-    const uint8_t* tab = tab_lds ? lds + ((sb + nk) % STAGES) * TL::SB : nullptr;
+    const RopeTab tab{tab_lds, ring + (uint32_t)((sb + nk) % STAGES) * TL::SB};
     sb = (sb + nk + STAGES - 1) % STAGES;  // the next tile's stage 0 avoids the table's slot
     vm_wait<0>();
     barrier();
@@ -833,9 +853,12 @@ hipError_t launch_qup_fwd_bf16(const FwdParams& p_in, hipStream_t stream) {
   FwdParams p = p_in;
   p.rope_lds = rope_rows_fit_lds(p);
   const dim3 grid(fwd_grid(p, device_cu_count()));
-  if (p.K % 64 == 0)
-    hipLaunchKernelGGL((qup_fwd_kernel<MODE_BF16, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
-  else
+  if (p.K % 64 == 0) {
+    if (p.rope_lds)
+      hipLaunchKernelGGL((qup_fwd_kernel<MODE_BF16, EPI_MLA, true>), grid, dim3(NTHREADS), 0, stream, p);
+    else
+      hipLaunchKernelGGL((qup_fwd_kernel<MODE_BF16, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
+  } else
     hipLaunchKernelGGL((qup_fwd_kernel<MODE_BF16_R64, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
@@ -844,10 +867,17 @@ hipError_t launch_qup_fwd_mx(const FwdParams& p_in, hipStream_t stream) {
   FwdParams p = p_in;
   p.rope_lds = rope_rows_fit_lds(p);
   const dim3 grid(fwd_grid(p, device_cu_count()));
-  if (p.mx_fp8_mfma)
-    hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_FP8, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
-  else
-    hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_EXACT, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
+  if (p.mx_fp8_mfma) {
+    if (p.rope_lds)
+      hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_FP8, EPI_MLA, true>), grid, dim3(NTHREADS), 0, stream, p);
+    else
+      hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_FP8, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
+  } else {
+    if (p.rope_lds)
+      hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_EXACT, EPI_MLA, true>), grid, dim3(NTHREADS), 0, stream, p);
+    else
+      hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_EXACT, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
