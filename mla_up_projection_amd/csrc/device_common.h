@@ -140,17 +140,23 @@ struct TokenMap {
   int nseq;
 };
 
-__device__ __forceinline__ void token_coords(const TokenMap& tm, int64_t t, int& pos, int& b,
-                                             int& s) {
-  const int t32 = (int)t;  // T < 2^31 (validated by the C ABI)
+// BSHD and SBHD (fmt one of the two): t = b S + s or t = s B + b.
+__device__ __forceinline__ void token_coords_dense(const TokenMap& tm, int t32, int& pos, int& b, int& s) {
   if (tm.fmt == FMT_BSHD) {
     b = t32 / tm.S;
     s = t32 - b * tm.S;
-    pos = s;
-  } else if (tm.fmt == FMT_SBHD) {
+  } else {
     s = t32 / tm.B;
     b = t32 - s * tm.B;
-    pos = s;
+  }
+  pos = s;
+}
+
+__device__ __forceinline__ void token_coords(const TokenMap& tm, int64_t t, int& pos, int& b,
+                                             int& s) {
+  const int t32 = (int)t;  // T < 2^31 (validated by the C ABI)
+  if (tm.fmt == FMT_BSHD || tm.fmt == FMT_SBHD) {
+    token_coords_dense(tm, t32, pos, b, s);
   } else {
     // largest j with cu[j] <= t (binary search over nseq+1 entries)
     int lo = 0, hi = tm.nseq;
@@ -162,6 +168,38 @@ __device__ __forceinline__ void token_coords(const TokenMap& tm, int64_t t, int&
     b = 0;
     s = t32;
   }
+}
+
+// token_coords for a lane whose token t lies in a run [base, last] that is
+// the same for the whole wave. For THD the sequence search then runs once per
+// wave on scalar loads, which count against lgkmcnt and so never wait for the
+// vector-memory loads (DMA) in flight, and each lane takes the last sequence
+// start at or before its token among the starts inside the run.
+__device__ __forceinline__ void token_coords_run(const TokenMap& tm, int64_t t, int base, int last, int& pos,
+                                                 int& b, int& s) {
+  if (tm.fmt == FMT_BSHD || tm.fmt == FMT_SBHD) {
+    token_coords_dense(tm, (int)t, pos, b, s);
+    return;
+  }
+  typedef __attribute__((address_space(4))) const int32_t cint32;
+  const cint32* cu = (const cint32*)tm.cu;
+  base = __builtin_amdgcn_readfirstlane(base);
+  last = __builtin_amdgcn_readfirstlane(last);
+  const int t32 = (int)t;
+  int lo = 0, hi = tm.nseq;  // largest j < nseq with cu[j] <= base
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= base) lo = mid; else hi = mid;
+  }
+  int start = cu[lo];
+  for (int j = lo + 1; j < tm.nseq; ++j) {  // sequence starts inside the run
+    const int c = cu[j];
+    if (c > last) break;
+    if (c <= t32) start = c;
+  }
+  pos = t32 - start;
+  b = 0;
+  s = t32;
 }
 
 }  // namespace mla

@@ -107,11 +107,14 @@ struct TokInfo {
   int64_t row;  // BHSD row of head 0: (b*H)*S + s; head h adds h*S
 };
 
-__device__ __forceinline__ TokInfo tok_info(const FwdParams& p, const TokenMap& tm, int64_t t) {
+// t: this lane's token, in the wave's run of 32 consecutive tokens starting at
+// t - (lane & 31).
+__device__ __forceinline__ TokInfo tok_info(const FwdParams& p, const TokenMap& tm, int64_t t, int lane) {
   TokInfo ti{t < p.T, 0, 0};
   if (ti.ok) {
     int b, s;
-    token_coords(tm, t, ti.pos, b, s);
+    const int base = (int)t - (lane & 31);
+    token_coords_run(tm, t, base, base + 31, ti.pos, b, s);
     ti.row = (int64_t)b * p.H * p.S + s;
   }
   return ti;
@@ -276,7 +279,7 @@ __device__ __forceinline__ void epilogue_tok(const FwdParams& p, const TokenMap&
                                              const f32x16_t (&acc)[WBLK_N][WBLK_T], int n0, int64_t t_lane,
                                              int lane, RopeTab tab, int tok0,
                                              std::integer_sequence<int, NBs...>) {
-  const TokInfo ti = tok_info(p, tm, t_lane + 32 * TB);
+  const TokInfo ti = tok_info(p, tm, t_lane + 32 * TB, lane);
   // When the tile is exactly one head, the head's D/32 scale bytes of this
   // token are contiguous: store them as 16-bit pairs, right after the token
   // row's codes, instead of one byte per block.
@@ -326,8 +329,10 @@ __device__ __forceinline__ void stage_rope_rows(const FwdParams& p, const TokenM
     const int r = 8 * j + (lane >> 3);
     int64_t t = t0 + r;
     if (t >= p.T) t = p.T - 1;
+    // the wave's run: rows 8j .. 8j + 7 (clamped like t)
+    const int run0 = (int)min(t0 + 8 * j, p.T - 1), run1 = (int)min(t0 + 8 * j + 7, p.T - 1);
     int pos, b, s;
-    token_coords(tm, t, pos, b, s);
+    token_coords_run(tm, t, run0, run1, pos, b, s);
     if (pos < 0 || pos >= p.rope_rows) pos = 0;
     const uint32_t off = (uint32_t)pos * (uint32_t)(p.rope_pairs * 4) + (uint32_t)(((lane & 7) ^ rope_swz(r)) * 16);
     dma16(p.cos, off, dst + j * 1024);
