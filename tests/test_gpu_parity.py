@@ -197,6 +197,18 @@ def test_fwd_thd_yarn_small():
                      yarn=(40.0, 4096, 32.0, 1.0, 1.0))
 
 
+def test_fwd_thd_many_short_and_empty_sequences():
+    """Sequences of 0 to 5 tokens among longer ones, across two token tiles:
+    32-token runs that hold several sequence starts (and empty sequences), so
+    every token must restart its position at its own sequence's start."""
+    lengths = [1, 0, 3, 5, 0, 2, 31, 33, 1, 1, 1, 64, 7, 0, 0, 4, 2, 2, 2, 2, 40, 1, 3, 0]
+    cu = syn.cu_seqlens_of(lengths)
+    T, K, H = sum(lengths), 128, 2
+    x = syn.normal_bf16((T, K), 1.0, 32)
+    w = syn.normal_bf16((H * 192, K), 0.05, 33)
+    full_compare_fwd(x, w, H=H, dn=128, dr=64, fmt=m.FMT_THD, cu=cu, max_seqlen=max(lengths))
+
+
 def test_fwd_mxfp8_projection_small():
     T, K, H = 300, 256, 3
     x = syn.normal_bf16((T, K), 1.0, 40)
