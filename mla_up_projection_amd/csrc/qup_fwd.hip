@@ -25,7 +25,7 @@
 //     STAGES-1 stages ahead; each wave counts its own outstanding loads with
 //     s_waitcnt vmcnt and one s_barrier per stage publishes the slot. The
 //     only other vector-memory loads in the loop are the MXFP8 operand
-//     scales, issued with the stage they belong to.
+//     scales, one dword per row for a pair of stages.
 //   * After the last stage of a tile, the first stages of the workgroup's
 //     next tile are put in flight before the epilogue runs.
 //   * Tiles are ordered so that the 64 workgroups resident on one XCD share
