@@ -724,10 +724,13 @@ def run_kv(kv, pe, *, H, dn, dr, dv, mx, fmt=m.FMT_BSHD, B=1, S=None, cu=None, m
     return key, val, ks, vs
 
 
-@pytest.mark.parametrize("fmt,B,S,lengths", [(m.FMT_BSHD, 1, 333, None), (m.FMT_SBHD, 3, 77, None),
-                                             (m.FMT_THD, 1, None, [64, 129, 7])])
-def test_kv_rope_against_oracle(fmt, B, S, lengths):
-    H, dn, dr, dv = 3, 128, 64, 128
+# the last case has a partial group of heads (64 + 6) and a partial chunk of
+# tokens (13 = 3 x 4 + 1) in the kernel's work split
+@pytest.mark.parametrize("fmt,B,S,lengths,H", [(m.FMT_BSHD, 1, 333, None, 3), (m.FMT_SBHD, 3, 77, None, 3),
+                                               (m.FMT_THD, 1, None, [64, 129, 7], 3),
+                                               (m.FMT_BSHD, 1, 13, None, 70)])
+def test_kv_rope_against_oracle(fmt, B, S, lengths, H):
+    dn, dr, dv = 128, 64, 128
     cu = syn.cu_seqlens_of(lengths) if lengths else None
     T = sum(lengths) if lengths else B * S
     max_pos = max(lengths) if lengths else S
