@@ -516,6 +516,84 @@ __device__ __forceinline__ PairScales unpack_pair(const StageScales& raw, int ha
   return ps;
 }
 
+// FP8 MFMA mode: scales in groups of four stages. For group j the lane in
+// wave half h loads the two dwords of stages 4j + 2h and 4j + 2h + 1 of each
+// row (one 8-byte load; two dword loads, each clamped, for a group that runs
+// past the last stage), two half-swaps give every lane all four stages, and
+// the bytes the lane passes (blocks h and 2 + h of each stage) pack into two
+// dwords: stages 4j, 4j + 1 in the first, 4j + 2, 4j + 3 in the second. A
+// quarter of the load instructions of one dword per lane and stage.
+struct QuadScales {
+  uint32_t w[WBLK_N][2];
+  uint32_t x[WBLK_T][2];
+};
+
+__device__ __forceinline__ QuadScales load_quad(const FwdParams& p, const ScaleRows& sr, int j, int nk, int half) {
+  QuadScales q;
+  const int kt = 4 * j + 2 * half;
+  if (4 * j + 3 < nk) {
+    const int k4 = 4 * kt;
+    const auto ld8 = [](const uint8_t* a, uint32_t (&o)[2]) {
+      u32x2_t v;  // 8 bytes at a 4-byte aligned address: one global_load_dwordx2
+      __builtin_memcpy(&v, a, 8);
+      o[0] = v[0];
+      o[1] = v[1];
+    };
+#pragma unroll
+    for (int nb = 0; nb < WBLK_N; ++nb) ld8(p.ws + sr.w[nb] + k4, q.w[nb]);
+#pragma unroll
+    for (int tb = 0; tb < WBLK_T; ++tb) ld8(p.xs + sr.x[tb] + k4, q.x[tb]);
+  } else {
+    const int ka = 4 * min(kt, nk - 1), kb = 4 * min(kt + 1, nk - 1);
+#pragma unroll
+    for (int nb = 0; nb < WBLK_N; ++nb) {
+      q.w[nb][0] = *reinterpret_cast<const uint32_t*>(p.ws + sr.w[nb] + ka);
+      q.w[nb][1] = *reinterpret_cast<const uint32_t*>(p.ws + sr.w[nb] + kb);
+    }
+#pragma unroll
+    for (int tb = 0; tb < WBLK_T; ++tb) {
+      q.x[tb][0] = *reinterpret_cast<const uint32_t*>(p.xs + sr.x[tb] + ka);
+      q.x[tb][1] = *reinterpret_cast<const uint32_t*>(p.xs + sr.x[tb] + kb);
+    }
+  }
+  return q;
+}
+
+__device__ __forceinline__ QuadScales unpack_quad(const QuadScales& raw, int half) {
+  QuadScales q;
+  const uint32_t sel = half ? 0x07050301u : 0x06040200u;
+  const auto one = [&](const uint32_t (&r)[2], uint32_t (&o)[2]) {
+    const u32x2_t t0 = swap_halves(r[0], r[0]);  // stages 4j, 4j + 2
+    const u32x2_t t1 = swap_halves(r[1], r[1]);  // stages 4j + 1, 4j + 3
+    o[0] = __builtin_amdgcn_perm(t1[0], t0[0], sel);
+    o[1] = __builtin_amdgcn_perm(t1[1], t0[1], sel);
+  };
+#pragma unroll
+  for (int nb = 0; nb < WBLK_N; ++nb) one(raw.w[nb], q.w[nb]);
+#pragma unroll
+  for (int tb = 0; tb < WBLK_T; ++tb) one(raw.x[tb], q.x[tb]);
+  return q;
+}
+
+__device__ __forceinline__ StageScales quad_stage(const QuadScales& q, int kt) {
+  // a select of two named values and a shift (a runtime index into the
+  // pair would put the arrays in scratch memory)
+  const bool hi = (kt >> 1) & 1;
+  const int sh = 16 * (kt & 1);
+  StageScales sc;
+#pragma unroll
+  for (int nb = 0; nb < WBLK_N; ++nb) {
+    const uint32_t a = q.w[nb][0], b = q.w[nb][1];
+    sc.w[nb] = (hi ? b : a) >> sh;
+  }
+#pragma unroll
+  for (int tb = 0; tb < WBLK_T; ++tb) {
+    const uint32_t a = q.x[tb][0], b = q.x[tb][1];
+    sc.x[tb] = (hi ? b : a) >> sh;
+  }
+  return sc;
+}
+
 // Scales of stage kt of the current pair.
 template <bool FP8>
 __device__ __forceinline__ StageScales stage_scales(const PairScales& ps, int kt) {
@@ -748,6 +826,8 @@ void qup_fwd_kernel(FwdParams p) {
   ScaleRows sr{};
   StageScales sc_raw{}, sc_cur{};
   PairScales sc_pair{};
+  QuadScales q_raw{}, q_cur{};  // FP8 MFMA mode
+  constexpr bool QUAD = MODE == MODE_MX_FP8;
   if (MX) sr = scale_rows(p, t0, n0, arow0, brow0, un_.kt0);
   // stage s of the current tile lives in slot (sb + s) % STAGES; each tile
   // starts where the previous one's stage sequence (nk + STAGES - 1 issued
@@ -761,7 +841,10 @@ void qup_fwd_kernel(FwdParams p) {
   static_assert(!TAB || (STAGES == 2 && EPI == EPI_MLA), "table staging uses the spare slot of a 2-slot ring");
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, sb + s, ring, wave);
-  if (MX) sc_raw = load_pair(p, sr, 0, nk, half);  // MX: STAGES == 2
+  if (QUAD)
+    q_raw = load_quad(p, sr, 0, nk, half);
+  else if (MX)
+    sc_raw = load_pair(p, sr, 0, nk, half);  // MX: STAGES == 2
 
   for (;;) {
     f32x16_t acc[WBLK_N][WBLK_T];
@@ -783,9 +866,16 @@ void qup_fwd_kernel(FwdParams p) {
         stage_rope_rows(p, tm, t0, ring + (uint32_t)((sb + nk) % STAGES) * TL::SB, wave, lane);
       else
         issue_stage<MODE>(dp, xb, wb, kt + STAGES - 1, nk, sb + kt + STAGES - 1, ring, wave);
-      if (MX) {
-        // pair kt / 2 arrived (the wait above covers all vector loads); the
-        // next pair goes out with stage kt + 1's DMA
+      if (QUAD) {
+        // group kt / 4 arrived (the wait above covers all vector loads); the
+        // next group goes out with stage kt + 1's DMA
+        if ((kt & 3) == 0) {
+          q_cur = unpack_quad(q_raw, half);
+          q_raw = load_quad(p, sr, kt / 4 + 1, nk, half);
+        }
+        sc_cur = quad_stage(q_cur, kt);
+      } else if (MX) {
+        // the same in pairs of stages
         if ((kt & 1) == 0) {
           sc_pair = unpack_pair<MODE == MODE_MX_FP8>(sc_raw, half);
           sc_raw = load_pair(p, sr, kt / 2 + 1, nk, half);
@@ -818,7 +908,10 @@ void qup_fwd_kernel(FwdParams p) {
       for (int s = 0; s < STAGES - 1; ++s) issue_stage<MODE>(dp, xb, wb, s, nk, sb + s, ring, wave);
       if (MX) {
         sr = scale_rows(p, t0, n0, arow0, brow0, un_.kt0);
-        sc_raw = load_pair(p, sr, 0, nk, half);
+        if (QUAD)
+          q_raw = load_quad(p, sr, 0, nk, half);
+        else
+          sc_raw = load_pair(p, sr, 0, nk, half);
       }
     }
     if (EPI == EPI_PLAIN)
