@@ -527,6 +527,12 @@ struct QuadScales {
   uint32_t w[WBLK_N][2];
   uint32_t x[WBLK_T][2];
 };
+// Exact mode: both wave halves pass all four bytes of a stage, so the four
+// stages' dwords are kept as loaded.
+struct QuadScales4 {
+  uint32_t w[WBLK_N][4];
+  uint32_t x[WBLK_T][4];
+};
 
 __device__ __forceinline__ QuadScales load_quad(const FwdParams& p, const ScaleRows& sr, int j, int nk, int half) {
   QuadScales q;
@@ -573,6 +579,39 @@ __device__ __forceinline__ QuadScales unpack_quad(const QuadScales& raw, int hal
 #pragma unroll
   for (int tb = 0; tb < WBLK_T; ++tb) one(raw.x[tb], q.x[tb]);
   return q;
+}
+
+__device__ __forceinline__ QuadScales4 unpack_quad4(const QuadScales& raw) {
+  QuadScales4 q;
+  const auto one = [&](const uint32_t (&r)[2], uint32_t (&o)[4]) {
+    const u32x2_t t0 = swap_halves(r[0], r[0]);  // stages 4j, 4j + 2
+    const u32x2_t t1 = swap_halves(r[1], r[1]);  // stages 4j + 1, 4j + 3
+    o[0] = t0[0];
+    o[1] = t1[0];
+    o[2] = t0[1];
+    o[3] = t1[1];
+  };
+#pragma unroll
+  for (int nb = 0; nb < WBLK_N; ++nb) one(raw.w[nb], q.w[nb]);
+#pragma unroll
+  for (int tb = 0; tb < WBLK_T; ++tb) one(raw.x[tb], q.x[tb]);
+  return q;
+}
+
+__device__ __forceinline__ StageScales quad4_stage(const QuadScales4& q, int kt) {
+  const bool hi = (kt >> 1) & 1, odd = kt & 1;
+  StageScales sc;
+#pragma unroll
+  for (int nb = 0; nb < WBLK_N; ++nb) {
+    const uint32_t a = odd ? q.w[nb][1] : q.w[nb][0], b = odd ? q.w[nb][3] : q.w[nb][2];
+    sc.w[nb] = hi ? b : a;
+  }
+#pragma unroll
+  for (int tb = 0; tb < WBLK_T; ++tb) {
+    const uint32_t a = odd ? q.x[tb][1] : q.x[tb][0], b = odd ? q.x[tb][3] : q.x[tb][2];
+    sc.x[tb] = hi ? b : a;
+  }
+  return sc;
 }
 
 __device__ __forceinline__ StageScales quad_stage(const QuadScales& q, int kt) {
@@ -826,8 +865,11 @@ void qup_fwd_kernel(FwdParams p) {
   ScaleRows sr{};
   StageScales sc_raw{}, sc_cur{};
   PairScales sc_pair{};
-  QuadScales q_raw{}, q_cur{};  // FP8 MFMA mode
-  constexpr bool QUAD = MODE == MODE_MX_FP8;
+  QuadScales q_raw{}, q_cur{};  // FP8 MFMA mode: packed bytes
+  QuadScales4 q4_cur{};         // exact mode: whole dwords
+  // groups of four stages, except the exact mode's fused forward, which has
+  // no registers to spare for them (pairs there)
+  constexpr bool QUAD = MODE == MODE_MX_FP8 || (MODE == MODE_MX_EXACT && EPI == EPI_PLAIN);
   if (MX) sr = scale_rows(p, t0, n0, arow0, brow0, un_.kt0);
   // stage s of the current tile lives in slot (sb + s) % STAGES; each tile
   // starts where the previous one's stage sequence (nk + STAGES - 1 issued
@@ -870,10 +912,13 @@ void qup_fwd_kernel(FwdParams p) {
         // group kt / 4 arrived (the wait above covers all vector loads); the
         // next group goes out with stage kt + 1's DMA
         if ((kt & 3) == 0) {
-          q_cur = unpack_quad(q_raw, half);
+          if (MODE == MODE_MX_FP8)
+            q_cur = unpack_quad(q_raw, half);
+          else
+            q4_cur = unpack_quad4(q_raw);
           q_raw = load_quad(p, sr, kt / 4 + 1, nk, half);
         }
-        sc_cur = quad_stage(q_cur, kt);
+        sc_cur = MODE == MODE_MX_FP8 ? quad_stage(q_cur, kt) : quad4_stage(q4_cur, kt);
       } else if (MX) {
         // the same in pairs of stages
         if ((kt & 1) == 0) {
