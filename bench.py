@@ -251,6 +251,29 @@ def main():
     parts["kv_rope_mxfp8_dsv3"] = {"ms": ms_kv, "gbs": kv_bytes / (ms_kv * 1e-3) / 1e9,
                                    "pct_hbm_peak": 100 * kv_bytes / (ms_kv * 1e-3) / 1e9 / HBM_PEAK_GBS}
     del kvin, kpe, kkey, kks, kval, kvs
+    # one rank's share under 8-way head (tensor) parallelism: the first 16
+    # heads of W (N = 3072), the same 4096 tokens, forward and backward
+    Hs = H // 8
+    Ns = Hs * D
+    w_s = w[:Ns]
+    dq_s = dq.reshape(T, H, D)[:, :Hs].contiguous()
+    out_s = torch.empty(1, Hs, T, D, dtype=torch.uint8, device=dev)
+    out_s_sc = torch.empty(1, Hs, T, D // 32, dtype=torch.uint8, device=dev)
+    dq_pre_s = torch.empty(T, Ns, dtype=torch.bfloat16, device=dev)
+    bkw_s = dict(H=Hs, d_nope=dn, d_rope=dr, cos=cos, sin=sin,
+                 dx=torch.empty(T, K, dtype=torch.bfloat16, device=dev),
+                 dw=torch.empty(Ns, K, dtype=torch.bfloat16, device=dev),
+                 db=torch.empty(Ns, dtype=torch.bfloat16, device=dev), use_bias=True, B=1, S=T)
+    ws_s = torch.empty(max(m.mla_qup_bwd_workspace_size(dq_s, x, w_s, dq_pre_s, **bkw_s), 1),
+                       dtype=torch.uint8, device=dev)
+    ms_fs = timed(lambda: m.mla_qup_fwd(x, w_s, out_s, H=Hs, d_nope=dn, d_rope=dr, cos=cos, sin=sin,
+                                        out_scales=out_s_sc, B=1, S=T), R)
+    ms_bs = timed(lambda: m.mla_qup_bwd(dq_s, x, w_s, dq_pre_s, workspace=ws_s, **bkw_s), R)
+    f_s = 2.0 * T * Ns * K
+    parts["qup_tp8_shard_16_heads"] = {
+        "fwd_ms": ms_fs, "fwd_tflops": f_s / (ms_fs * 1e-3) / 1e12,
+        "bwd_ms": ms_bs, "bwd_tflops": 2 * f_s / (ms_bs * 1e-3) / 1e12}
+    del dq_s, out_s, out_s_sc, dq_pre_s, bkw_s, ws_s
     # context: the vendor library GEMM (torch -> hipBLASLt) on the same three
     # products, bf16 out, with no epilogue and no inverse RoPE
     dq2 = dq.reshape(T, N)

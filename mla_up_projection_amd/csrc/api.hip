@@ -331,7 +331,7 @@ size_t mla_qup_bwd_workspace_size(const mla_qup_bwd_args* a) {
   int64_t max_pos = 0;
   if (check_bwd_shapes(a, &max_pos) != MLA_OK) return 0;
   const int N = a->H * (a->d_nope + a->d_rope);
-  return mla::plan_bwd(a->tokens.T, N, a->K, a->use_bias != 0, a->dx != nullptr).total;
+  return mla::plan_bwd(a->tokens.T, N, a->K, a->use_bias != 0, a->dx != nullptr, a->dw != nullptr).total;
 }
 
 static bool mx_bwd_shapes_ok(int64_t T, int N, int K) {
@@ -374,7 +374,7 @@ static mla_status qup_bwd_impl(const mla_qup_bwd_args* a, int mx, int fp8_mfma, 
       (a->db && !aligned(a->db, 2)))
     return MLA_EINVAL;
   if (mx && !mx_bwd_shapes_ok(T, N, a->K)) return MLA_EUNSUPPORTED;
-  mla::BwdPlan plan = mla::plan_bwd(T, N, a->K, a->use_bias != 0, a->dx != nullptr);
+  mla::BwdPlan plan = mla::plan_bwd(T, N, a->K, a->use_bias != 0, a->dx != nullptr, a->dw != nullptr);
   mla::MxBwdPlan mplan{};
   if (mx) {
     mplan = mla::plan_bwd_mx(T, N, a->K, a->use_bias != 0);

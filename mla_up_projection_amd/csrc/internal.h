@@ -58,10 +58,13 @@ struct BwdParams {
 
 // Workspace plan of the backward: byte offsets into the caller's workspace.
 struct BwdPlan {
-  int db_row_chunks;       // token chunks of the db partial sums
+  int ir_rows;             // token rows per inverse-RoPE workgroup (8..64)
+  int db_row_chunks;       // token chunks of the db partial sums (one per such row band)
   size_t db_off, db_bytes;
   int dx_splits;           // reduction splits of the dX GEMM (1 = none)
   size_t dx_off, dx_bytes;
+  int dw_splits;           // reduction (token) splits of the dW GEMM (1 = none)
+  size_t dw_off, dw_bytes;
   size_t total;
 };
 // MXFP8 backward workspace: the bf16 backward's db partials, then the
@@ -77,7 +80,7 @@ struct MxBwdPlan {
   size_t dx_part;
   size_t total;
 };
-BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx);
+BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx, bool want_dw);
 
 // Compute units of the current device (cached per device; 0 if unknown).
 int device_cu_count();

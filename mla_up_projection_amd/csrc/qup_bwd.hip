@@ -15,7 +15,8 @@
 //                     reach LDS by DMA in memory order, and an operand whose
 //                     reduction axis is strided in memory is transposed by the
 //                     LDS transpose read (ds_read_b64_tr_b16).
-//   split_reduce_kernel: ordered sum of the dX reduction splits -> bf16.
+//   split_reduce_kernel: ordered sum of the reduction splits of dX (long N)
+//                     or dW (few heads, long T) -> bf16 or fp32.
 //   launch_qup_bwd_mx: the MXFP8 backward (operands quantized along each
 //                     product's reduction axis, products on the forward
 //                     kernel's MXFP8 main loop).
@@ -33,17 +34,17 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int IR_THREADS = 128;
 constexpr int IR_COLS = IR_THREADS * 8;  // columns per workgroup
-constexpr int IR_ROWS = 64;              // token rows per workgroup
+constexpr int IR_ROWS = 64;              // token rows per workgroup, at most
 
 // RQ: also quantize each dq_pre row along n from its bf16 copy (the MXFP8
 // backward's dX operand): the four lanes of a 32-column block share its amax
 // through two xor-shuffles; codes [T, N] and scales [T, N/32].
 template <bool RQ>
-__global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, float* __restrict__ db_part,
+__global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, int band, float* __restrict__ db_part,
                                                               uint8_t* __restrict__ rc, uint8_t* __restrict__ rs) {
   __shared__ int s_pos[IR_ROWS];
-  const int64_t r0 = (int64_t)blockIdx.y * IR_ROWS;
-  const int rows = (int)min((int64_t)IR_ROWS, p.T - r0);
+  const int64_t r0 = (int64_t)blockIdx.y * band;  // band <= IR_ROWS token rows
+  const int rows = (int)min((int64_t)band, p.T - r0);
   const TokenMap tm{p.fmt, p.B, p.S, p.cu, p.nseq};
   for (int i = threadIdx.x; i < rows; i += IR_THREADS) {
     int pos, b, s;
@@ -593,8 +594,11 @@ int bg_grid(const BGemm& g, int cus) {
   return (int)(tiles < n ? tiles : n);
 }
 
+// Sum of the fp32 partials of the reduction splits, in split order, rounded
+// once to the output type (bf16, or fp32 with F32OUT).
+template <bool F32OUT>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int splits,
-                                                          int64_t n4, uint16_t* __restrict__ out) {
+                                                          int64_t n4, void* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   float4 s = reinterpret_cast<const float4*>(part)[i];
@@ -602,7 +606,10 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
     const float4 v = reinterpret_cast<const float4*>(part + (int64_t)z * n4 * 4)[i];
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
-  reinterpret_cast<uint2*>(out)[i] = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+  if (F32OUT)
+    reinterpret_cast<float4*>(out)[i] = s;
+  else
+    reinterpret_cast<uint2*>(out)[i] = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int64_t words) {
@@ -623,17 +630,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-// Reduction splits of the dX GEMM: the split count s (1..8) whose rounds of
-// resident workgroups cover the work in the least time, ceil(tiles s / slots)
-// rounds of ceil(stages / s) stages, preferring fewer splits (each split adds
-// an fp32 partial of dX to write and reduce) and at least 8 stages per split.
-// Reduction values per stage of the dX GEMM: 64 (whole 128-byte lines of
-// dq_pre per row) when N allows it.
-static int dx_stage_depth(int N) { return N % 64 == 0 ? 64 : 32; }
-
-static int dx_split_count(int64_t T, int N, int K) {
-  const int64_t tiles = ((T + BG_TJ - 1) / BG_TJ) * ((K + BG_TI - 1) / BG_TI);
-  const int64_t stages = N / dx_stage_depth(N);
+// Reduction splits of a backward GEMM: the split count s (1..8) whose rounds
+// of resident workgroups cover the work in the least time, ceil(tiles s /
+// slots) rounds of ceil(stages / s) stages, preferring fewer splits (each
+// split adds an fp32 partial of the output to write and reduce) and at least
+// 8 stages per split.
+static int split_count(int64_t tiles, int64_t stages) {
   const int cus = device_cu_count();
   const int64_t slots = (int64_t)(cus > 0 ? cus : 256) * BG_WG_PER_CU;
   int best = 1;
@@ -651,15 +653,63 @@ static int dx_split_count(int64_t T, int N, int K) {
   return (int)((stages + sps - 1) / sps);  // no empty split
 }
 
-BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx) {
+// Reduction values per stage of the dX GEMM: 64 (whole 128-byte lines of
+// dq_pre per row) when N allows it.
+static int dx_stage_depth(int N) { return N % 64 == 0 ? 64 : 32; }
+
+static int dx_split_count(int64_t T, int N, int K) {
+  const int64_t tiles = ((T + BG_TJ - 1) / BG_TJ) * ((K + BG_TI - 1) / BG_TI);
+  return split_count(tiles, N / dx_stage_depth(N));
+}
+
+// dW reduces over the tokens, 64 per stage; with few heads (N / 128 row
+// tiles) its tiles alone cannot fill the chip. Its output is large, so the
+// split count weighs the partials too: a round of stages takes about 1.3 us,
+// and each split's fp32 partial (N K 4 bytes) is written once and read once
+// by the reduction at about 6 TB/s.
+static int dw_split_count(int64_t T, int N, int K) {
+  const int64_t tiles = (int64_t)((N + BG_TJ - 1) / BG_TJ) * ((K + BG_TI - 1) / BG_TI);
+  const int64_t stages = (T + 63) / 64;
+  const int cus = device_cu_count();
+  const int64_t slots = (int64_t)(cus > 0 ? cus : 256) * BG_WG_PER_CU;
+  const double stage_us = 1.3, part_us = (double)N * K * 8 / 6e6;
+  int best = 1;
+  double best_cost = (double)((tiles + slots - 1) / slots) * stages * stage_us;
+  for (int s = 2; s <= 8; ++s) {
+    const int64_t sps = (stages + s - 1) / s;
+    if (sps < 8) break;
+    const double cost = (double)((tiles * s + slots - 1) / slots) * sps * stage_us + s * part_us;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  const int64_t sps = (stages + best - 1) / best;
+  return (int)((stages + sps - 1) / sps);  // no empty split
+}
+
+BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx, bool want_dw) {
   BwdPlan pl{};
-  pl.db_row_chunks = (int)((T + IR_ROWS - 1) / IR_ROWS);
+  // Rows per inverse-RoPE workgroup: the most (up to 64) that still give
+  // 1536 workgroups, the count that runs at copy speed at DeepSeek-V3 shape
+  // (with few heads, 64-row bands leave most of the chip idle).
+  const int64_t col_blocks = (N + IR_COLS - 1) / IR_COLS;
+  pl.ir_rows = 8;
+  for (int r = IR_ROWS; r > 8; r /= 2)
+    if (col_blocks * ((T + r - 1) / r) >= 1536) {
+      pl.ir_rows = r;
+      break;
+    }
+  pl.db_row_chunks = (int)((T + pl.ir_rows - 1) / pl.ir_rows);
   pl.db_off = 0;
   pl.db_bytes = use_bias ? align256((size_t)pl.db_row_chunks * N * 4) : 0;
   pl.dx_splits = want_dx && T > 0 ? dx_split_count(T, N, K) : 1;
   pl.dx_off = pl.db_bytes;
   pl.dx_bytes = pl.dx_splits > 1 ? align256((size_t)pl.dx_splits * T * K * 4) : 0;
-  pl.total = pl.db_bytes + pl.dx_bytes;
+  pl.dw_splits = want_dw && T > 0 ? dw_split_count(T, N, K) : 1;
+  pl.dw_off = pl.dx_off + pl.dx_bytes;
+  pl.dw_bytes = pl.dw_splits > 1 ? align256((size_t)pl.dw_splits * N * K * 4) : 0;
+  pl.total = pl.db_bytes + pl.dx_bytes + pl.dw_bytes;
   return pl;
 }
 
@@ -673,7 +723,8 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
   float* db_part = p.use_bias ? reinterpret_cast<float*>(ws + pl.db_off) : nullptr;
   {
     dim3 grid((p.N + IR_COLS - 1) / IR_COLS, pl.db_row_chunks);
-    hipLaunchKernelGGL(inv_rope_kernel<false>, grid, dim3(IR_THREADS), 0, stream, p, db_part, nullptr, nullptr);
+    hipLaunchKernelGGL(inv_rope_kernel<false>, grid, dim3(IR_THREADS), 0, stream, p, pl.ir_rows, db_part, nullptr,
+                       nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -713,7 +764,7 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     if (e != hipSuccess) return e;
     if (split) {
       const int64_t n4 = p.T * p.K / 4;
-      hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+      hipLaunchKernelGGL(split_reduce_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
                          static_cast<const float*>(g.out), g.splits, n4, p.dx);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -729,15 +780,30 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     g.I = p.K;
     g.J = p.N;
     g.R = p.T;
-    g.splits = 1;
-    g.sps = (int)((p.T + 63) / 64);
-    g.out = p.dw;
-    if (p.dw_fp32)
+    const int stages = (int)((p.T + 63) / 64);
+    g.splits = pl.dw_splits;
+    g.sps = (stages + g.splits - 1) / g.splits;
+    // split: fp32 partials [splits][N][K] in the workspace, summed below
+    const bool split = g.splits > 1;
+    g.out = split ? static_cast<void*>(ws + pl.dw_off) : p.dw;
+    if (split || p.dw_fp32)
       hipLaunchKernelGGL((bgemm_kernel<false, 64, true>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
     else
       hipLaunchKernelGGL((bgemm_kernel<false, 64, false>), dim3(bg_grid(g, cus)), dim3(BG_THREADS), 0, stream, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (split) {
+      const int64_t n4 = (int64_t)p.N * p.K / 4;
+      const dim3 rg((unsigned)((n4 + 255) / 256));
+      if (p.dw_fp32)
+        hipLaunchKernelGGL(split_reduce_kernel<true>, rg, dim3(256), 0, stream,
+                           static_cast<const float*>(g.out), g.splits, n4, p.dw);
+      else
+        hipLaunchKernelGGL(split_reduce_kernel<false>, rg, dim3(256), 0, stream,
+                           static_cast<const float*>(g.out), g.splits, n4, p.dw);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
@@ -776,7 +842,7 @@ static int mx_split_count(int64_t tiles, int64_t stages) {
 
 MxBwdPlan plan_bwd_mx(int64_t T, int N, int K, bool use_bias) {
   MxBwdPlan pl{};
-  pl.base = plan_bwd(T, N, K, use_bias, false);
+  pl.base = plan_bwd(T, N, K, use_bias, false, false);
   pl.Tp = (T + 127) / 128 * 128;
   size_t off = pl.base.total;
   auto take = [&](size_t bytes) {
@@ -807,7 +873,7 @@ hipError_t launch_qup_bwd_mx(const BwdParams& p, const MxBwdPlan& pl, int fp8_mf
   // in one pass; the quantization along t reads the stored dq_pre below
   float* db_part = p.use_bias ? reinterpret_cast<float*>(ws + pl.base.db_off) : nullptr;
   hipLaunchKernelGGL(inv_rope_kernel<true>, dim3((N + IR_COLS - 1) / IR_COLS, pl.base.db_row_chunks),
-                     dim3(IR_THREADS), 0, stream, p, db_part, ws + pl.dq_rows, ws + pl.dq_rows_sc);
+                     dim3(IR_THREADS), 0, stream, p, pl.base.ir_rows, db_part, ws + pl.dq_rows, ws + pl.dq_rows_sc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.use_bias) {
@@ -839,7 +905,7 @@ hipError_t launch_qup_bwd_mx(const BwdParams& p, const MxBwdPlan& pl, int fp8_mf
     if ((e = launch_mx_gemm(g, stream))) return e;
     if (split) {
       const int64_t n4 = T * K / 4;
-      hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+      hipLaunchKernelGGL(split_reduce_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
                          reinterpret_cast<const float*>(ws + pl.dx_part), pl.dx_splits, n4, p.dx);
       if ((e = hipGetLastError())) return e;
     }

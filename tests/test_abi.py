@@ -164,6 +164,33 @@ def test_bwd_workspace_size(L):
     assert L.mla_qup_bwd_workspace_size(ctypes.byref(bwd_args(K=10))) == 0
 
 
+def test_bwd_workspace_holds_dw_token_splits(L):
+    # H = 2 (N = 384), K = 192: 3 dW output tiles. T = 1000 is 16 token stages
+    # of 64 (2 splits of 8), T = 2000 is 32 (4 splits of 8): fp32 partials
+    # [splits, N, K] in the workspace, none when dW is not requested.
+    N, K = 384, 192
+    for T, s in ((1000, 2), (2000, 4)):
+        kw = dict(H=2, K=K, tokens__T=T, tokens__S=T, rope__rows=T, use_bias=0, dx=0)
+        assert L.mla_qup_bwd_workspace_size(ctypes.byref(bwd_args(**kw))) == s * N * K * 4
+        assert L.mla_qup_bwd_workspace_size(ctypes.byref(bwd_args(**kw, dw=0))) == 0
+    # 16 heads (one rank of 8-way head parallelism), T = 4096: 192 tiles, 2 splits
+    kw = dict(H=16, tokens__T=4096, tokens__S=4096, rope__rows=4096, use_bias=0, dx=0)
+    assert L.mla_qup_bwd_workspace_size(ctypes.byref(bwd_args(**kw))) == 2 * 3072 * 1536 * 4
+    # all 128 heads: 1536 tiles fill the chip, no split
+    kw = dict(H=128, tokens__T=4096, tokens__S=4096, rope__rows=4096, use_bias=0, dx=0)
+    assert L.mla_qup_bwd_workspace_size(ctypes.byref(bwd_args(**kw))) == 0
+
+
+def test_bwd_workspace_db_bands(L):
+    # db partials: one fp32 column-sum row per token band of the inverse-RoPE
+    # grid, whose band is the most rows (64, 32, 16 or 8) that still give 1536
+    # workgroups of 1024 columns. 128 heads (24 column blocks), T = 4096: 64-row
+    # bands; 16 heads (3 column blocks): 8-row bands.
+    for H, band in ((128, 64), (16, 8)):
+        kw = dict(H=H, tokens__T=4096, tokens__S=4096, rope__rows=4096, dx=0, dw=0)
+        assert L.mla_qup_bwd_workspace_size(ctypes.byref(bwd_args(**kw))) == (4096 // band) * H * 192 * 4
+
+
 @pytest.mark.parametrize("over,code", [
     (dict(db=0), bd.MLA_EINVAL),                 # use_bias without a db buffer
     (dict(use_bias=2), bd.MLA_EINVAL),
@@ -182,14 +209,17 @@ def test_bwd_validation(L, over, code):
 
 
 def test_bwd_mxfp8_workspace_and_validation(L):
-    # T = 256, N = 4 * 192 = 768, K = 1536: db partials, then the quantized operands,
-    # each 256-byte aligned (all of these sizes already are); dX needs no split here
-    # (16 tiles, 6 stages of 128).
+    # T = 256, N = 4 * 192 = 768, K = 1536: db partials (one column-sum row per
+    # 8-token band: a single 1024-column block leaves the inverse-RoPE grid short
+    # of 1536 workgroups even at 8 rows, the smallest band), then the quantized
+    # operands, each 256-byte aligned (all of these sizes already are); dX needs
+    # no split here (16 tiles, 6 stages of 128).
     T, N, K = 256, 768, 1536
-    expect = (4 * N * 4) + T * N + T * N // 32 + N * T + N * T // 32 + K * N + K * N // 32 \
+    db_part = (T // 8) * N * 4
+    expect = db_part + T * N + T * N // 32 + N * T + N * T // 32 + K * N + K * N // 32 \
         + K * T + K * T // 32
     assert L.mla_qup_bwd_mxfp8_workspace_size(ctypes.byref(bwd_args())) == expect
-    assert L.mla_qup_bwd_mxfp8_workspace_size(ctypes.byref(bwd_args(use_bias=0))) == expect - 4 * N * 4
+    assert L.mla_qup_bwd_mxfp8_workspace_size(ctypes.byref(bwd_args(use_bias=0))) == expect - db_part
     # N = 3 * 192 = 576 is not a multiple of 128
     assert L.mla_qup_bwd_mxfp8_workspace_size(ctypes.byref(bwd_args(H=3))) == 0
     assert L.mla_qup_bwd_mxfp8(ctypes.byref(bwd_args(H=3)), 0, None) == bd.MLA_EUNSUPPORTED

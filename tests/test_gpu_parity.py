@@ -385,6 +385,25 @@ def test_bwd_small_against_oracle():
         assert frob_rel(o.to_f64(g["db"].cpu()), r.db) <= 1e-2
 
 
+@pytest.mark.parametrize("T", [1000, 2000])
+def test_bwd_dw_token_splits(T):
+    """Few heads, many tokens: dW has 3 x 1 output tiles, so its token
+    reduction is split (2 splits of 8 stages at T = 1000, 4 at T = 2000; the
+    last split ends in a partial stage) and the fp32 partials are summed in
+    split order, into bf16 and into fp32 dW."""
+    K, H = 192, 2
+    x = syn.normal_bf16((T, K), 1.0, 63)
+    w = syn.normal_bf16((H * 192, K), 0.02, 64)
+    dq = syn.normal_bf16((T, H, 192), 1e-3, 65)
+    for dw_fp32 in (False, True):
+        g = run_bwd(dq, x, w, H=H, dn=128, dr=64, S=T, dw_fp32=dw_fp32)
+        r = o.qup_backward(dq, x, w, H=H, d_nope=128, d_rope=64, cos=g["oc"], sin=g["os"], S=T)
+        check_bf16(bits16(g["dq_pre"]), o.f32_to_bf16_bits(r.dq_pre.astype(np.float32)), "dq_pre")
+        assert frob_rel(o.to_f64(g["dx"].cpu()), r.dx) <= 1e-2
+        assert frob_rel(o.to_f64(g["dw"].cpu()), r.dw) <= 1e-2
+        assert frob_rel(o.to_f64(g["db"].cpu()), r.db) <= 1e-2
+
+
 def test_bwd_thd_yarn_no_bias():
     lengths = [64, 129, 7]
     cu = syn.cu_seqlens_of(lengths)
@@ -655,6 +674,32 @@ def test_bwd_full_size_sampled():
     nrows = sample_rows(N, seed=7)
     dw_ref = dq_pre[:, nrows].T @ xf
     assert frob_rel(o.to_f64(g["dw"][torch.from_numpy(nrows).to(DEV)].cpu()), dw_ref) <= 1e-2
+    assert frob_rel(o.to_f64(g["db"].cpu()), dq_pre.sum(0)) <= 1e-2
+
+
+def test_bwd_tp8_shard_sampled():
+    """One rank's share under 8-way head parallelism at DeepSeek-V3 size: the
+    first 16 heads (N = 3072), T = 4096, K = 1536, in the launch configuration
+    the benchmark times (dW in 2 token splits). Sampled dX and dW rows, all of
+    db."""
+    wl = syn.workload("dsv3_bwd")
+    Hs = wl.H // 8
+    T, K, D = wl.T, wl.K, wl.D
+    Ns = Hs * D
+    x = wl.x()
+    w = wl.w()[:Ns].contiguous()
+    dq = wl.dq().reshape(T, wl.H, D)[:, :Hs].contiguous()
+    g = run_bwd(dq, x, w, H=Hs, dn=wl.d_nope, dr=wl.d_rope, S=wl.S, use_bias=True)
+    pos, _, _ = o.token_coords(o.FMT_BSHD, T, 1, T)
+    dq_pre = o.rope_rotate(o.to_f64(dq), pos, g["oc"], g["os"], wl.d_nope, wl.d_rope,
+                           inverse=True).reshape(T, Ns)
+    rows = sample_rows(T)
+    check_bf16(bits16(g["dq_pre"][torch.from_numpy(rows).to(DEV)]),
+               o.f32_to_bf16_bits(dq_pre[rows].astype(np.float32)), "dq_pre")
+    wf, xf = o.to_f64(w), o.to_f64(x)
+    assert frob_rel(o.to_f64(g["dx"][torch.from_numpy(rows).to(DEV)].cpu()), dq_pre[rows] @ wf) <= 1e-2
+    nrows = sample_rows(Ns, seed=7)
+    assert frob_rel(o.to_f64(g["dw"][torch.from_numpy(nrows).to(DEV)].cpu()), dq_pre[:, nrows].T @ xf) <= 1e-2
     assert frob_rel(o.to_f64(g["db"].cpu()), dq_pre.sum(0)) <= 1e-2
 
 
