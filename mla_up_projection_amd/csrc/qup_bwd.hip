@@ -10,7 +10,8 @@
 //   inv_rope_kernel : dq [T,N] -> dq_pre [T,N] (bf16), adjoint rotation of
 //                     each rope pair; per-chunk fp32 column sums for db.
 //                     HBM-bound: 2 B read + 2 B written per element.
-//   db_reduce_kernel: db[n] = sum over chunks, in chunk order.
+//   db_reduce_kernel: db[n] = sum over chunks in a fixed order (per-lane
+//                     strided sums, then lane order).
 //   bgemm_kernel    : dX = dq_pre W and dW = dq_pre^T X on bf16 MFMA; operands
 //                     reach LDS by DMA in memory order, and an operand whose
 //                     reduction axis is strided in memory is transposed by the
@@ -160,26 +161,38 @@ __global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, int b
   }
 }
 
-// db[n] = sum of the per-chunk partials, in chunk order: 8 lanes per column
-// each add every 8th chunk, then the 8 partial sums are added in lane order.
+// db[n] = sum of the per-chunk partials in a fixed order: G lanes per column
+// each add every G-th chunk, then the G partial sums are added in lane order.
+// G = 8, or 32 when there are many chunks (short token bands) so that each
+// lane's serial chain stays short.
 constexpr int DBR_COLS = 32;
-__global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict__ part, int chunks,
-                                                       int N, uint16_t* __restrict__ db) {
-  __shared__ float red[8][DBR_COLS];
+template <int G>
+__global__ __launch_bounds__(DBR_COLS * G) void db_reduce_kernel(const float* __restrict__ part, int chunks,
+                                                                int N, uint16_t* __restrict__ db) {
+  __shared__ float red[G][DBR_COLS];
   const int c = threadIdx.x % DBR_COLS;
   const int g = threadIdx.x / DBR_COLS;
   const int n = blockIdx.x * DBR_COLS + c;
   float s = 0.0f;
   if (n < N)
-    for (int k = g; k < chunks; k += 8) s += part[(int64_t)k * N + n];
+    for (int k = g; k < chunks; k += G) s += part[(int64_t)k * N + n];
   red[g][c] = s;
   __syncthreads();
   if (g == 0 && n < N) {
     float t = red[0][c];
 #pragma unroll
-    for (int q = 1; q < 8; ++q) t += red[q][c];
+    for (int q = 1; q < G; ++q) t += red[q][c];
     db[n] = (uint16_t)f32_to_bf16_bits(t);
   }
+}
+
+hipError_t launch_db_reduce(const float* part, int chunks, int N, uint16_t* db, hipStream_t stream) {
+  const dim3 grid((N + DBR_COLS - 1) / DBR_COLS);
+  if (chunks >= 128)
+    hipLaunchKernelGGL(db_reduce_kernel<32>, grid, dim3(DBR_COLS * 32), 0, stream, part, chunks, N, db);
+  else
+    hipLaunchKernelGGL(db_reduce_kernel<8>, grid, dim3(DBR_COLS * 8), 0, stream, part, chunks, N, db);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -729,9 +742,7 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     if (e != hipSuccess) return e;
   }
   if (p.use_bias) {
-    hipLaunchKernelGGL(db_reduce_kernel, dim3((p.N + DBR_COLS - 1) / DBR_COLS), dim3(256), 0, stream, db_part,
-                       pl.db_row_chunks, p.N, p.db);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_db_reduce(db_part, pl.db_row_chunks, p.N, p.db, stream);
     if (e != hipSuccess) return e;
   }
   const int cus = device_cu_count();
@@ -877,9 +888,7 @@ hipError_t launch_qup_bwd_mx(const BwdParams& p, const MxBwdPlan& pl, int fp8_mf
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.use_bias) {
-    hipLaunchKernelGGL(db_reduce_kernel, dim3((N + DBR_COLS - 1) / DBR_COLS), dim3(256), 0, stream, db_part,
-                       pl.base.db_row_chunks, N, p.db);
-    if ((e = hipGetLastError())) return e;
+    if ((e = launch_db_reduce(db_part, pl.base.db_row_chunks, N, p.db, stream))) return e;
   }
   if (p.dx) {
     if ((e = launch_mxfp8_quantize_t(p.w, N, K, K, N, ws + pl.w_t, ws + pl.w_t_sc, stream))) return e;
