@@ -166,10 +166,11 @@ def test_bwd_workspace_size(L):
 
 def test_bwd_workspace_holds_dw_token_splits(L):
     # H = 2 (N = 384), K = 192: 3 dW output tiles. T = 1000 is 16 token stages
-    # of 64 (2 splits of 8), T = 2000 is 32 (4 splits of 8): fp32 partials
-    # [splits, N, K] in the workspace, none when dW is not requested.
+    # of 64 (2 splits of 8), T = 1500 is 24 (3 of 8), T = 2000 is 32 (4 of 8):
+    # fp32 partials [splits, N, K] in the workspace, none when dW is not
+    # requested.
     N, K = 384, 192
-    for T, s in ((1000, 2), (2000, 4)):
+    for T, s in ((1000, 2), (1500, 3), (2000, 4)):
         kw = dict(H=2, K=K, tokens__T=T, tokens__S=T, rope__rows=T, use_bias=0, dx=0)
         assert L.mla_qup_bwd_workspace_size(ctypes.byref(bwd_args(**kw))) == s * N * K * 4
         assert L.mla_qup_bwd_workspace_size(ctypes.byref(bwd_args(**kw, dw=0))) == 0

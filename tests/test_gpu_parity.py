@@ -404,6 +404,26 @@ def test_bwd_dw_token_splits(T):
         assert frob_rel(o.to_f64(g["db"].cpu()), r.db) <= 1e-2
 
 
+def test_bwd_dw_token_splits_thd_dw_only():
+    """dW alone (no dX, no bias: the split partials start the workspace) over a
+    packed THD batch with YaRN, T = 1500: 24 stages of 64 tokens in 3 splits of
+    8, sequence starts inside the splits, and a partial last stage."""
+    lengths = [700, 1, 333, 466]
+    cu = syn.cu_seqlens_of(lengths)
+    T, K, H = sum(lengths), 192, 2
+    x = syn.normal_bf16((T, K), 1.0, 66)
+    w = syn.normal_bf16((H * 192, K), 0.02, 67)
+    dq = syn.normal_bf16((T, H, 192), 1e-3, 68)
+    yarn = (40.0, 4096, 32.0, 1.0, 1.0)
+    for dw_fp32 in (False, True):
+        g = run_bwd(dq, x, w, H=H, dn=128, dr=64, fmt=m.FMT_THD, cu=cu, max_seqlen=max(lengths),
+                    use_bias=False, yarn=yarn, want=("dw",), dw_fp32=dw_fp32)
+        r = o.qup_backward(dq, x, w, H=H, d_nope=128, d_rope=64, cos=g["oc"], sin=g["os"],
+                           fmt=o.FMT_THD, cu_seqlens=cu.numpy())
+        check_bf16(bits16(g["dq_pre"]), o.f32_to_bf16_bits(r.dq_pre.astype(np.float32)), "dq_pre")
+        assert frob_rel(o.to_f64(g["dw"].cpu()), r.dw) <= 1e-2
+
+
 def test_bwd_thd_yarn_no_bias():
     lengths = [64, 129, 7]
     cu = syn.cu_seqlens_of(lengths)
