@@ -225,8 +225,12 @@ typedef struct {
   size_t workspace_bytes;
 } mla_qup_bwd_args;
 
-/* Workspace bytes mla_qup_bwd needs for these shapes (0 if none); reads only
- * the shape fields, never dereferences pointers. Returns 0 for invalid shapes. */
+/* Workspace bytes mla_qup_bwd needs for these arguments (0 if none): the db
+ * partial sums when use_bias, and the fp32 partials of dX or dW when their
+ * reduction is split (long N for dX; few heads and many tokens for dW), so it
+ * depends on which of dx, dw and db are requested: query it with the same
+ * arguments as the call. Reads the shape fields and whether dx / dw are NULL,
+ * never dereferences pointers. Returns 0 for invalid shapes. */
 MLA_API size_t mla_qup_bwd_workspace_size(const mla_qup_bwd_args* args);
 
 /* Errors: MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EWORKSPACE,
