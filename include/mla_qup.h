@@ -103,7 +103,11 @@ typedef struct {
   double mscale;        /* multiplier of cos and sin */
 } mla_yarn;
 
-/* RoPE table: cos[p*pairs + i], sin[p*pairs + i], fp32, device. */
+/* RoPE table: cos[p*pairs + i], sin[p*pairs + i], fp32, device, each
+ * 16-byte aligned (the inverse-RoPE kernel reads four pairs with one 16-byte
+ * load, the forward epilogue two with one 8-byte load). Forward page,
+ * flowchart: "RoPE cos/sin" is an input of the fused up-projection; YaRN-fix
+ * page, Problem: the table must cover the rope width and every position. */
 typedef struct {
   const float* cos;
   const float* sin;
@@ -172,7 +176,8 @@ typedef struct {
   const void* w;            /* BF16 [N, K] or MXFP8 codes [N, K]; 16-B aligned */
   const uint8_t* w_scales;  /* MXFP8: [N, K/32], 4-B aligned; else NULL */
   int32_t w_dtype;          /* must equal x_dtype */
-  const void* bias;         /* bf16 [N] added before the rotation, or NULL */
+  const void* bias;         /* bf16 [N] added before the rotation, or NULL;
+                               8-B aligned */
   int32_t K;                /* q_lora_rank; > 0, multiple of 32 (MXFP8: of 128) */
   int32_t H;                /* heads, > 0 */
   int32_t d_nope;           /* >= 0, even */
@@ -195,7 +200,15 @@ typedef struct {
  * output RMS on MX-scaled data. Ignored for bf16 operands. */
 enum { MLA_FWD_FP8_MFMA = 1 };
 
-/* Errors: MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EUNSUPPORTED
+/* The fused forward. Forward page, description: the Q up-projection GEMM
+ * with the RoPE that follows it and MXFP8 quantization of the query in one
+ * kernel, BF16 or MXFP8 projection; flowchart: X, W and RoPE cos/sin in,
+ * MXFP8 Q with BHSD scale transpose out; YaRN-fix page, Changes: YaRN RoPE
+ * on q in sbhd and thd formats, the input left unmodified.
+ * Ownership: every pointer is caller-owned device memory; inputs are read
+ * only; out and out_scales are written completely (every element of the
+ * [B, H, S, D] output).
+ * Errors: MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EUNSUPPORTED
  * (x_dtype != w_dtype, or X or W spanning more than 4 GiB: the kernel
  * addresses their rows with 32-bit offsets), MLA_EDEVICE. */
 MLA_API mla_status mla_qup_fwd(const mla_qup_fwd_args* args, void* stream);
@@ -225,7 +238,10 @@ typedef struct {
   size_t workspace_bytes;
 } mla_qup_bwd_args;
 
-/* Workspace bytes mla_qup_bwd needs for these arguments (0 if none): the db
+/* Workspace bytes mla_qup_bwd needs for these arguments (0 if none). Backward
+ * page, review comment on the missing bias gradient and sequence diagram
+ * (linear backward for input and weight gradients): the workspace holds the
+ * partial sums of those reductions. It contains the db
  * partial sums when use_bias, and the fp32 partials of dX or dW when their
  * reduction is split (long N for dX; few heads and many tokens for dW), so it
  * depends on which of dx, dw and db are requested: query it with the same
@@ -233,7 +249,14 @@ typedef struct {
  * never dereferences pointers. Returns 0 for invalid shapes. */
 MLA_API size_t mla_qup_bwd_workspace_size(const mla_qup_bwd_args* args);
 
-/* Errors: MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EWORKSPACE,
+/* The backward. Backward page, summary and sequence diagram: the RoPE
+ * backward turns the query-output gradient into the pre-RoPE projection
+ * gradient, then the linear backward gives the input and weight gradients;
+ * review comment: with use_bias the bias gradient is produced. YaRN-fix
+ * page, review thread: the weight gradient is dy^T x with x the saved input.
+ * Ownership: caller-owned device memory; dq, x, w and the table are read
+ * only; dq_pre, dx, dw, db and the workspace are written.
+ * Errors: MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EWORKSPACE,
  * MLA_EDEVICE. */
 MLA_API mla_status mla_qup_bwd(const mla_qup_bwd_args* args, void* stream);
 

@@ -114,12 +114,42 @@ def _check(status: int, where: str) -> None:
         raise MlaError(status, where)
 
 
-def _ptr(t) -> int | None:
-    if t is None:
-        return None
-    if not t.is_contiguous():
-        raise ValueError("tensors passed to libmlaqup must be contiguous")
-    return t.data_ptr()
+# Device type every tensor argument must live on (the library receives raw
+# device pointers and cannot tell a host address from a device one).
+DEVICE_TYPE = "cuda"
+
+_BF16, _FP32, _U8, _I32 = torch.bfloat16, torch.float32, torch.uint8, torch.int32
+
+
+class _Dev:
+    """Checks of one call's tensor arguments before any pointer crosses the C
+    ABI: every tensor on one device of DEVICE_TYPE, contiguous, of an
+    accepted dtype and with the element count the C call will assume."""
+
+    def __init__(self, where: str):
+        self.where = where
+        self.device = None
+
+    def __call__(self, t, name: str, dtypes, numel=None, min_numel=None) -> int | None:
+        if t is None:
+            return None
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{self.where}: {name} must be a torch tensor")
+        if t.device.type != DEVICE_TYPE:
+            raise ValueError(f"{self.where}: {name} is on {t.device}, not on the GPU")
+        if self.device is None:
+            self.device = t.device
+        elif t.device != self.device:
+            raise ValueError(f"{self.where}: {name} is on {t.device}, other arguments on {self.device}")
+        if t.dtype not in dtypes:
+            raise ValueError(f"{self.where}: {name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.where}: {name} must be contiguous")
+        if numel is not None and t.numel() != numel:
+            raise ValueError(f"{self.where}: {name} has {t.numel()} elements, expected {numel}")
+        if min_numel is not None and t.numel() < min_numel:
+            raise ValueError(f"{self.where}: {name} has {t.numel()} elements, at least {min_numel} needed")
+        return t.data_ptr()
 
 
 def _stream(stream) -> int | None:
@@ -128,13 +158,13 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _tokens(T, fmt, B, S, cu_seqlens, max_seqlen) -> mla_tokens:
+def _tokens(chk: _Dev, T, fmt, B, S, cu_seqlens, max_seqlen) -> mla_tokens:
     tk = mla_tokens()
     tk.fmt = fmt
     tk.T = T
     if fmt == FMT_THD:
         tk.B, tk.S = 1, T
-        tk.cu_seqlens = _ptr(cu_seqlens)
+        tk.cu_seqlens = chk(cu_seqlens, "cu_seqlens", (_I32,), min_numel=2)
         tk.nseq = cu_seqlens.numel() - 1 if cu_seqlens is not None else 0
         tk.max_seqlen = int(max_seqlen) if max_seqlen is not None else 0
     else:
@@ -143,12 +173,14 @@ def _tokens(T, fmt, B, S, cu_seqlens, max_seqlen) -> mla_tokens:
     return tk
 
 
-def _rope(cos, sin, d_rope) -> mla_rope:
+def _rope(chk: _Dev, cos, sin, d_rope) -> mla_rope:
     r = mla_rope()
-    if cos is not None:
-        r.cos, r.sin = _ptr(cos), _ptr(sin)
+    if cos is not None or sin is not None:
+        if cos is None or sin is None or cos.dim() != 2 or cos.shape != sin.shape:
+            raise ValueError(f"{chk.where}: cos and sin must be two tables of one shape [rows, pairs]")
+        r.cos, r.sin = chk(cos, "cos", (_FP32,)), chk(sin, "sin", (_FP32,))
         r.rows = cos.shape[0]
-        r.pairs = cos.shape[1] if cos.dim() == 2 else d_rope // 2
+        r.pairs = cos.shape[1]
     return r
 
 
@@ -165,7 +197,11 @@ def rope_cache_build(cos, sin, d_rope: int, base: float = 10000.0, yarn=None, st
     """Fill fp32 device tables cos/sin [rows, d_rope/2]; yarn = (factor, L,
     beta_fast, beta_slow, mscale) or None."""
     y = _yarn(yarn)
-    st = lib().rope_cache_build(_ptr(cos), _ptr(sin), cos.shape[0], d_rope, float(base),
+    chk = _Dev("rope_cache_build")
+    if cos.dim() != 2 or cos.shape != sin.shape or cos.shape[1] != d_rope // 2:
+        raise ValueError("rope_cache_build: cos and sin must both be [rows, d_rope/2]")
+    pc, ps = chk(cos, "cos", (_FP32,)), chk(sin, "sin", (_FP32,))
+    st = lib().rope_cache_build(pc, ps, cos.shape[0], d_rope, float(base),
                                 ctypes.byref(y) if y is not None else None, _stream(stream))
     _check(st, "rope_cache_build")
 
@@ -173,11 +209,18 @@ def rope_cache_build(cos, sin, d_rope: int, base: float = 10000.0, yarn=None, st
 def mxfp8_quantize(x, codes, scales, stream=None):
     """x [rows, cols] bf16/fp32 (row stride may exceed cols) -> codes uint8
     [rows, cols], scales uint8 [rows, cols/32]."""
-    if x.stride(-1) != 1:
-        raise ValueError("x rows must be contiguous")
-    dt = DTYPE_FP32 if x.dtype == torch.float32 else DTYPE_BF16 if x.dtype == torch.bfloat16 else -1
-    st = lib().mxfp8_quantize(x.data_ptr(), dt, x.shape[0], x.shape[1], x.stride(0),
-                              _ptr(codes), _ptr(scales), _stream(stream))
+    chk = _Dev("mxfp8_quantize")
+    if x.dim() != 2 or x.stride(-1) != 1:
+        raise ValueError("mxfp8_quantize: x must be 2-D with contiguous rows")
+    rows, cols = x.shape
+    # x may be a row-strided view: check it as the rows it spans
+    span = x.as_strided(((rows - 1) * x.stride(0) + cols,) if rows else (0,), (1,))
+    px = chk(span, "x", (_BF16, _FP32))
+    dt = DTYPE_FP32 if x.dtype == torch.float32 else DTYPE_BF16
+    pc = chk(codes, "codes", (_U8,), numel=rows * cols)
+    psc = chk(scales, "scales", (_U8,), numel=rows * cols // 32)
+    st = lib().mxfp8_quantize(px if rows else x.data_ptr(), dt, rows, cols, x.stride(0), pc, psc,
+                              _stream(stream))
     _check(st, "mxfp8_quantize")
 
 
@@ -185,31 +228,44 @@ def mxfp8_quantize_t(x, codes_t, scales_t, rows_pad=None, stream=None):
     """x bf16 [rows, cols] (row stride may exceed cols) -> codes_t uint8
     [cols, rows_pad], scales_t uint8 [cols, rows_pad/32]: quantized along the
     columns, stored transposed; rows_pad defaults to codes_t.shape[1]."""
-    if x.stride(-1) != 1:
-        raise ValueError("x rows must be contiguous")
-    if x.dtype != torch.bfloat16:
-        raise ValueError("x must be bf16")
+    chk = _Dev("mxfp8_quantize_t")
+    if x.dim() != 2 or x.stride(-1) != 1:
+        raise ValueError("mxfp8_quantize_t: x must be 2-D with contiguous rows")
+    rows, cols = x.shape
+    span = x.as_strided(((rows - 1) * x.stride(0) + cols,) if rows else (0,), (1,))
+    px = chk(span, "x", (_BF16,))
     rp = codes_t.shape[1] if rows_pad is None else rows_pad
-    st = lib().mxfp8_quantize_t(x.data_ptr(), x.shape[0], x.shape[1], x.stride(0), rp,
-                                _ptr(codes_t), _ptr(scales_t), _stream(stream))
+    pc = chk(codes_t, "codes_t", (_U8,), numel=cols * rp)
+    psc = chk(scales_t, "scales_t", (_U8,), numel=cols * rp // 32)
+    st = lib().mxfp8_quantize_t(px if rows else x.data_ptr(), rows, cols, x.stride(0), rp, pc, psc,
+                                _stream(stream))
     _check(st, "mxfp8_quantize_t")
 
 
 def make_fwd_args(x, w, out, *, H, d_nope, d_rope, cos=None, sin=None, x_scales=None,
                   w_scales=None, bias=None, out_scales=None, fmt=FMT_BSHD, B=1, S=None,
                   cu_seqlens=None, max_seqlen=None, fp8_mfma=False) -> mla_qup_fwd_args:
+    chk = _Dev("mla_qup_fwd")
     a = mla_qup_fwd_args()
     a.flags = MLA_FWD_FP8_MFMA if fp8_mfma else 0
+    if x.dim() != 2:
+        raise ValueError("mla_qup_fwd: x must be [T, K]")
+    T, K = x.shape
+    N = H * (d_nope + d_rope)
     mx_in = x.dtype == torch.uint8
-    a.x, a.x_scales, a.x_dtype = _ptr(x), _ptr(x_scales), DTYPE_MXFP8 if mx_in else DTYPE_BF16
-    a.w, a.w_scales = _ptr(w), _ptr(w_scales)
+    a.x = chk(x, "x", (_BF16, _U8))
+    a.x_scales = chk(x_scales, "x_scales", (_U8,), numel=T * K // 32)
+    a.x_dtype = DTYPE_MXFP8 if mx_in else DTYPE_BF16
+    a.w = chk(w, "w", (_BF16, _U8), numel=N * K)
+    a.w_scales = chk(w_scales, "w_scales", (_U8,), numel=N * K // 32)
     a.w_dtype = DTYPE_MXFP8 if w.dtype == torch.uint8 else DTYPE_BF16
-    a.bias = _ptr(bias)
-    a.K, a.H, a.d_nope, a.d_rope = x.shape[1], H, d_nope, d_rope
-    a.tokens = _tokens(x.shape[0], fmt, B, S, cu_seqlens, max_seqlen)
-    a.rope = _rope(cos, sin, d_rope)
+    a.bias = chk(bias, "bias", (_BF16,), numel=N)
+    a.K, a.H, a.d_nope, a.d_rope = K, H, d_nope, d_rope
+    a.tokens = _tokens(chk, T, fmt, B, S, cu_seqlens, max_seqlen)
+    a.rope = _rope(chk, cos, sin, d_rope)
     a.out_dtype = DTYPE_MXFP8 if out.dtype == torch.uint8 else DTYPE_BF16
-    a.out, a.out_scales = _ptr(out), _ptr(out_scales)
+    a.out = chk(out, "out", (_BF16, _U8), numel=T * N)
+    a.out_scales = chk(out_scales, "out_scales", (_U8,), numel=T * N // 32)
     return a
 
 
@@ -225,17 +281,27 @@ def mla_qup_fwd(x, w, out, *, stream=None, **kw):
 def make_bwd_args(dq, x, w, dq_pre, *, H, d_nope, d_rope, cos=None, sin=None, dx=None, dw=None,
                   db=None, use_bias=False, workspace=None, fmt=FMT_BSHD, B=1, S=None,
                   cu_seqlens=None, max_seqlen=None) -> mla_qup_bwd_args:
+    chk = _Dev("mla_qup_bwd")
     a = mla_qup_bwd_args()
-    a.dq, a.x, a.w = _ptr(dq), _ptr(x), _ptr(w)
-    a.K, a.H, a.d_nope, a.d_rope = x.shape[1], H, d_nope, d_rope
-    a.tokens = _tokens(x.shape[0], fmt, B, S, cu_seqlens, max_seqlen)
-    a.rope = _rope(cos, sin, d_rope)
-    a.dq_pre, a.dx, a.dw = _ptr(dq_pre), _ptr(dx), _ptr(dw)
+    if x.dim() != 2:
+        raise ValueError("mla_qup_bwd: x must be [T, K]")
+    T, K = x.shape
+    N = H * (d_nope + d_rope)
+    a.dq = chk(dq, "dq", (_BF16,), numel=T * N)
+    a.x = chk(x, "x", (_BF16,))
+    a.w = chk(w, "w", (_BF16,), numel=N * K)
+    a.K, a.H, a.d_nope, a.d_rope = K, H, d_nope, d_rope
+    a.tokens = _tokens(chk, T, fmt, B, S, cu_seqlens, max_seqlen)
+    a.rope = _rope(chk, cos, sin, d_rope)
+    a.dq_pre = chk(dq_pre, "dq_pre", (_BF16,), numel=T * N)
+    a.dx = chk(dx, "dx", (_BF16,), numel=T * K)
+    a.dw = chk(dw, "dw", (_BF16, _FP32), numel=N * K)
     a.dw_dtype = DTYPE_FP32 if (dw is not None and dw.dtype == torch.float32) else DTYPE_BF16
     a.use_bias = 1 if use_bias else 0
-    a.db = _ptr(db)
+    a.db = chk(db, "db", (_BF16,), numel=N)
     if workspace is not None:
-        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+        a.workspace = chk(workspace, "workspace", (_U8,))
+        a.workspace_bytes = workspace.numel()
     return a
 
 
@@ -276,11 +342,19 @@ def mla_kv_rope(kv, k_pe, key, value, *, H, d_nope, d_rope, d_v, cos=None, sin=N
     """KV side: kv bf16 [T,H,d_nope+d_v], k_pe bf16 [T,d_rope] -> key [B,H,S,d_nope+d_rope]
     and value [B,H,S,d_v] (BHSD; THD: B=1, S=T), bf16 or uint8 E4M3 codes with
     key_scales / value_scales uint8 [.., D/32]."""
+    chk = _Dev("mla_kv_rope")
     a = mla_kv_args()
-    a.kv, a.k_pe = _ptr(kv), _ptr(k_pe)
+    T = kv.shape[0]
+    Dk, Dv = d_nope + d_rope, d_v
+    a.kv = chk(kv, "kv", (_BF16,), numel=T * H * (d_nope + d_v))
+    a.k_pe = chk(k_pe, "k_pe", (_BF16,), numel=T * d_rope)
     a.H, a.d_nope, a.d_rope, a.d_v = H, d_nope, d_rope, d_v
-    a.tokens = _tokens(kv.shape[0], fmt, B, S, cu_seqlens, max_seqlen)
-    a.rope = _rope(cos, sin, d_rope)
-    a.out_dtype = DTYPE_MXFP8 if key.dtype == torch.uint8 else DTYPE_BF16
-    a.key, a.key_scales, a.value, a.value_scales = _ptr(key), _ptr(key_scales), _ptr(value), _ptr(value_scales)
+    a.tokens = _tokens(chk, T, fmt, B, S, cu_seqlens, max_seqlen)
+    a.rope = _rope(chk, cos, sin, d_rope)
+    out_dt = key.dtype if key is not None else value.dtype
+    a.out_dtype = DTYPE_MXFP8 if out_dt == torch.uint8 else DTYPE_BF16
+    a.key = chk(key, "key", (out_dt,), numel=T * H * Dk)
+    a.value = chk(value, "value", (out_dt,), numel=T * H * Dv)
+    a.key_scales = chk(key_scales, "key_scales", (_U8,), numel=T * H * Dk // 32)
+    a.value_scales = chk(value_scales, "value_scales", (_U8,), numel=T * H * Dv // 32)
     _check(lib().mla_kv_rope(ctypes.byref(a), _stream(stream)), "mla_kv_rope")

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libmlaqup.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "rope_cache.hip", "mxfp8_quant.hip", "qup_fwd.hip", "qup_bwd.hip", "kv_rope.hip"]
+SOURCES = ["api.hip", "plan.hip", "rope_cache.hip", "mxfp8_quant.hip", "qup_fwd.hip", "qup_bwd.hip", "kv_rope.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",

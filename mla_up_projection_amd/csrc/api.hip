@@ -76,7 +76,9 @@ mla_status check_tokens(const mla_tokens& tk, int64_t* max_pos) {
 mla_status check_rope(const mla_rope& r, int32_t d_rope, int64_t max_pos) {
   if (d_rope == 0) return MLA_OK;
   if (r.cos == nullptr || r.sin == nullptr) return MLA_EINVAL;
-  if (!aligned(r.cos, 4) || !aligned(r.sin, 4)) return MLA_EINVAL;
+  // the inverse-RoPE kernel reads four table pairs with one 16-byte load and
+  // the forward epilogue two with one 8-byte load (when pairs % 4 == 0)
+  if (!aligned(r.cos, 16) || !aligned(r.sin, 16)) return MLA_EINVAL;
   if (r.pairs < d_rope / 2) return MLA_EROPE_TABLE;
   if ((int64_t)r.rows < max_pos + 1 || r.rows < 1) return MLA_EROPE_TABLE;
   return MLA_OK;
@@ -184,8 +186,9 @@ mla_status mxfp8_quantize_t(const void* x, int64_t rows, int64_t cols, int64_t l
 mla_status mla_kv_rope(const mla_kv_args* a, void* stream) {
   if (a == nullptr) return MLA_EINVAL;
   if (a->H < 1 || a->d_nope < 0 || a->d_rope < 0 || a->d_v < 0) return MLA_EINVAL;
-  if (a->d_nope % 8 || a->d_rope % 8 || a->d_v % 8 || a->d_nope + a->d_rope + a->d_v == 0) return MLA_EINVAL;
-  if (a->H > 65536 || a->d_nope + a->d_rope + a->d_v > 65536 || a->d_rope > 256) return MLA_EINVAL;
+  const int64_t widths = (int64_t)a->d_nope + a->d_rope + a->d_v;
+  if (a->d_nope % 8 || a->d_rope % 8 || a->d_v % 8 || widths == 0) return MLA_EINVAL;
+  if (a->H > 65536 || widths > 65536 || a->d_rope > 256) return MLA_EINVAL;
   if (a->out_dtype != MLA_DTYPE_BF16 && a->out_dtype != MLA_DTYPE_MXFP8) return MLA_EINVAL;
   const bool mx = a->out_dtype == MLA_DTYPE_MXFP8;
   const int Dk = a->d_nope + a->d_rope, Dv = a->d_v;
@@ -211,7 +214,7 @@ mla_status mla_kv_rope(const mla_kv_args* a, void* stream) {
     ins.push_back(rng(a->rope.sin, rope_bytes(a->rope, a->d_rope)));
   }
   if (a->tokens.fmt == MLA_FMT_THD)
-    ins.push_back(rng(a->tokens.cu_seqlens, (size_t)(a->tokens.nseq + 1) * 4));
+    ins.push_back(rng(a->tokens.cu_seqlens, ((size_t)a->tokens.nseq + 1) * 4));
   std::vector<Range> outs;
   if (Dk) outs.push_back(rng(a->key, TH * Dk * eo));
   if (Dv) outs.push_back(rng(a->value, TH * Dv * eo));
@@ -264,7 +267,8 @@ mla_status mla_qup_fwd(const mla_qup_fwd_args* a, void* stream) {
   if (mx_in && (a->x_scales == nullptr || a->w_scales == nullptr)) return MLA_EINVAL;
   if (mx_out && a->out_scales == nullptr) return MLA_EINVAL;
   if (!aligned(a->x, 16) || !aligned(a->w, 16) || !aligned(a->out, 16)) return MLA_EINVAL;
-  if (a->bias && !aligned(a->bias, 2)) return MLA_EINVAL;
+  // the epilogue reads four consecutive bias values with one 8-byte load
+  if (a->bias && !aligned(a->bias, 8)) return MLA_EINVAL;
   // each lane loads four consecutive scale bytes of a row as one dword
   if (mx_in && (!aligned(a->x_scales, 4) || !aligned(a->w_scales, 4))) return MLA_EINVAL;
 
@@ -286,7 +290,7 @@ mla_status mla_qup_fwd(const mla_qup_fwd_args* a, void* stream) {
     ins.push_back(rng(a->rope.sin, rope_bytes(a->rope, a->d_rope)));
   }
   if (a->tokens.fmt == MLA_FMT_THD)
-    ins.push_back(rng(a->tokens.cu_seqlens, (size_t)(a->tokens.nseq + 1) * 4));
+    ins.push_back(rng(a->tokens.cu_seqlens, ((size_t)a->tokens.nseq + 1) * 4));
   std::vector<Range> outs = {rng(a->out, (size_t)T * N * eout)};
   if (mx_out) outs.push_back(rng(a->out_scales, (size_t)T * N / 32));
   if (overlaps(outs, ins)) return MLA_EALIAS;
@@ -392,7 +396,7 @@ static mla_status qup_bwd_impl(const mla_qup_bwd_args* a, int mx, int fp8_mfma, 
     ins.push_back(rng(a->rope.sin, rope_bytes(a->rope, a->d_rope)));
   }
   if (a->tokens.fmt == MLA_FMT_THD)
-    ins.push_back(rng(a->tokens.cu_seqlens, (size_t)(a->tokens.nseq + 1) * 4));
+    ins.push_back(rng(a->tokens.cu_seqlens, ((size_t)a->tokens.nseq + 1) * 4));
   std::vector<Range> outs = {rng(a->dq_pre, (size_t)T * N * 2)};
   if (a->dx) outs.push_back(rng(a->dx, (size_t)T * a->K * 2));
   if (a->dw) outs.push_back(rng(a->dw, (size_t)N * a->K * (a->dw_dtype == MLA_DTYPE_FP32 ? 4 : 2)));

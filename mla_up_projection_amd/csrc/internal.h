@@ -9,6 +9,16 @@
 
 namespace mla {
 
+// Work decomposition shared by the kernels and the host planner (plan.hip).
+constexpr int FWD_TILE_T = 128;           // forward tile: tokens
+constexpr int FWD_TILE_N = 192;           // forward tile: rows of N
+constexpr int IR_THREADS = 128;           // inverse-RoPE workgroup
+constexpr int IR_COLS = IR_THREADS * 8;   // its columns
+constexpr int IR_ROWS = 64;               // its token rows, at most
+constexpr int BG_TI = 192;                // backward GEMM tile: output columns
+constexpr int BG_TJ = 128;                // backward GEMM tile: output rows
+constexpr int BG_WG_PER_CU = 2;           // backward GEMM workgroups per CU
+
 struct FwdParams {
   const void* x;           // bf16 [T,K] or e4m3 codes [T,K]
   const uint8_t* xs;       // MXFP8 x scales [T,K/32]
@@ -81,6 +91,8 @@ struct MxBwdPlan {
   size_t total;
 };
 BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx, bool want_dw);
+// Reduction values per stage of the dX product (64, or 32 when N % 64 != 0).
+int dx_stage_depth(int N);
 
 // Compute units of the current device (cached per device; 0 if unknown).
 int device_cu_count();

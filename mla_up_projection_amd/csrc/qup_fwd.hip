@@ -38,8 +38,8 @@
 namespace mla {
 namespace {
 
-constexpr int TILE_T = 128;
-constexpr int TILE_N = 192;                // one DeepSeek-V3 head (D = 192)
+constexpr int TILE_T = FWD_TILE_T;         // 128 tokens
+constexpr int TILE_N = FWD_TILE_N;         // 192 rows of N: one DeepSeek-V3 head (D = 192)
 constexpr int NTHREADS = 256;
 constexpr int WBLK_N = 3;                 // 32-row blocks of N per wave (96 rows)
 constexpr int WBLK_T = 2;                 // 32-token blocks per wave (64 tokens)
@@ -1022,10 +1022,6 @@ hipError_t launch_qup_fwd_mx(const FwdParams& p_in, hipStream_t stream) {
       hipLaunchKernelGGL((qup_fwd_kernel<MODE_MX_EXACT, EPI_MLA>), grid, dim3(NTHREADS), 0, stream, p);
   }
   return hipGetLastError();
-}
-
-int mx_gemm_tiles(int64_t rows, int cols) {
-  return (int)(((rows + TILE_T - 1) / TILE_T) * ((cols + TILE_N - 1) / TILE_N));
 }
 
 hipError_t launch_mx_gemm(const FwdParams& p, hipStream_t stream) {

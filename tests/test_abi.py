@@ -7,6 +7,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import mla_up_projection_amd as m
 from mla_up_projection_amd import binding as bd
@@ -113,6 +114,10 @@ def fwd(L, **over):
     (dict(out=addr(1, 4096)), bd.MLA_EALIAS),             # output inside x
     (dict(out_scales=addr(5, 64)), bd.MLA_EALIAS),        # scales inside out
     (dict(out=addr(3)), bd.MLA_EALIAS),                   # output over the cos table
+    (dict(rope__cos=addr(3, 4)), bd.MLA_EINVAL),          # table 4-B aligned: 16 needed
+    (dict(rope__sin=addr(4, 8)), bd.MLA_EINVAL),
+    (dict(bias=addr(11, 2)), bd.MLA_EINVAL),              # bias 2-B aligned: 8 needed
+    (dict(bias=addr(11, 4)), bd.MLA_EINVAL),
 ])
 def test_fwd_validation(L, over, code):
     assert fwd(L, **over) == code
@@ -134,6 +139,10 @@ def test_fwd_validation_mx_and_thd(L):
     # zero tokens: valid, nothing enqueued (no GPU needed)
     assert fwd(L, tokens__T=0, tokens__S=0, tokens__B=1) == bd.MLA_EINVAL  # S < 1
     assert fwd(L, **{**thd, "tokens__T": 0}) == bd.MLA_OK
+    # the table check runs before the zero-token return: 16-byte aligned
+    # tables are accepted, 4- and 8-byte aligned ones are not
+    assert fwd(L, **{**thd, "tokens__T": 0, "rope__cos": addr(3, 16), "rope__sin": addr(4, 48)}) == bd.MLA_OK
+    assert fwd(L, **{**thd, "tokens__T": 0, "rope__cos": addr(3, 8)}) == bd.MLA_EINVAL
 
 
 def bwd_args(**over):
@@ -204,6 +213,8 @@ def test_bwd_workspace_db_bands(L):
     (dict(dx=addr(1, 512)), bd.MLA_EALIAS),      # dx inside dq
     (dict(dw=addr(6, 1024)), bd.MLA_EALIAS),     # dw inside dq_pre
     (dict(db=addr(10, 4096)), bd.MLA_EALIAS),    # db inside the workspace
+    (dict(rope__cos=addr(4, 4)), bd.MLA_EINVAL),  # table rows read 16 bytes at a time
+    (dict(rope__sin=addr(5, 8)), bd.MLA_EINVAL),
 ])
 def test_bwd_validation(L, over, code):
     assert L.mla_qup_bwd(ctypes.byref(bwd_args(**over)), None) == code
@@ -275,6 +286,7 @@ def kv_args(**over):
     (dict(value=addr(5, 4096)), bd.MLA_EALIAS),          # value inside key
     (dict(value_scales=addr(2, 64)), bd.MLA_EALIAS),     # scales inside k_pe
     (dict(tokens__T=0, tokens__S=1, tokens__B=1), bd.MLA_EINVAL),  # B*S != T
+    (dict(rope__cos=addr(3, 4)), bd.MLA_EINVAL),         # tables 16-byte aligned
 ])
 def test_kv_rope_validation(L, over, code):
     assert L.mla_kv_rope(ctypes.byref(kv_args(**over)), None) == code
@@ -308,3 +320,100 @@ def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(bd, "LIB_PATH", "/nonexistent/libmlaqup.so")
     with pytest.raises(RuntimeError, match="missing"):
         bd.lib()
+
+
+# ------------------------------------------------- binding argument checks --
+# The binding checks every tensor before a pointer crosses the C ABI, which
+# cannot tell a host address or a short buffer from a good one. "meta" tensors
+# stand in for device tensors here (no GPU, no data).
+@pytest.fixture
+def meta(monkeypatch):
+    monkeypatch.setattr(bd, "DEVICE_TYPE", "meta")
+    return lambda *shape, dt=torch.bfloat16, dev="meta": torch.empty(*shape, dtype=dt, device=dev)
+
+
+def _fwd_kw(t, T=64, K=64, H=2, dn=16, dr=16):
+    D = dn + dr
+    return dict(x=t(T, K), w=t(H * D, K), out=t(1, H, T, D, dt=torch.uint8),
+                out_scales=t(1, H, T, D // 32, dt=torch.uint8), cos=t(T, dr // 2, dt=torch.float32),
+                sin=t(T, dr // 2, dt=torch.float32), H=H, d_nope=dn, d_rope=dr, B=1, S=T)
+
+
+def test_binding_rejects_host_cu_seqlens(meta):
+    kw = _fwd_kw(meta)
+    kw.update(fmt=bd.FMT_THD, S=None, max_seqlen=64)
+    cu_host = torch.tensor([0, 30, 64], dtype=torch.int32)          # built on the CPU
+    x, w, out = kw.pop("x"), kw.pop("w"), kw.pop("out")
+    with pytest.raises(ValueError, match="cu_seqlens is on cpu"):
+        m.mla_qup_fwd(x, w, out, cu_seqlens=cu_host, **kw)
+    # an int64 cu_seqlens on the device is refused too (the kernels read int32)
+    with pytest.raises(ValueError, match="cu_seqlens has dtype torch.int64"):
+        m.mla_qup_fwd(x, w, out, cu_seqlens=meta(3, dt=torch.int64), **kw)
+
+
+@pytest.mark.parametrize("name,shape,dt", [
+    ("out", (1, 2, 63, 32), torch.uint8),         # one token row short
+    ("out_scales", (1, 2, 64, 0), torch.uint8),
+    ("w", (63, 64), torch.bfloat16),              # fewer than H*D rows
+    ("w", (64, 64), torch.float16),               # wrong dtype
+    ("cos", (64, 8), torch.float16),
+])
+def test_binding_rejects_undersized_or_mistyped_fwd_tensors(meta, name, shape, dt):
+    kw = _fwd_kw(meta)
+    kw[name] = meta(*shape, dt=dt)
+    if name == "cos":
+        kw["sin"] = meta(*shape, dt=dt)
+    x, w, out = kw.pop("x"), kw.pop("w"), kw.pop("out")
+    with pytest.raises(ValueError, match=name):
+        m.mla_qup_fwd(x, w, out, **kw)
+
+
+def test_binding_rejects_host_tensor_and_mixed_devices(meta):
+    kw = _fwd_kw(meta)
+    x, w, out = kw.pop("x"), kw.pop("w"), kw.pop("out")
+    with pytest.raises(ValueError, match="x is on cpu"):
+        m.mla_qup_fwd(torch.empty(64, 64, dtype=torch.bfloat16), w, out, **kw)
+    with pytest.raises(ValueError, match="not contiguous|contiguous"):
+        m.mla_qup_fwd(meta(64, 128)[:, ::2], w, out, **kw)
+
+
+@pytest.mark.parametrize("name,shape,dt", [
+    ("dq_pre", (64, 63), torch.bfloat16),
+    ("dx", (64, 32), torch.bfloat16),
+    ("dw", (64, 64), torch.float16),
+    ("db", (32,), torch.bfloat16),
+    ("workspace", (16,), torch.float32),
+])
+def test_binding_rejects_bad_bwd_tensors(meta, name, shape, dt):
+    T, K, H, dn, dr = 64, 64, 2, 16, 16
+    N = H * (dn + dr)
+    args = dict(dq=meta(T, H, dn + dr), x=meta(T, K), w=meta(N, K), dq_pre=meta(T, N))
+    kw = dict(H=H, d_nope=dn, d_rope=dr, cos=meta(T, dr // 2, dt=torch.float32),
+              sin=meta(T, dr // 2, dt=torch.float32), dx=meta(T, K), dw=meta(N, K), db=meta(N),
+              use_bias=True, workspace=meta(1024, dt=torch.uint8), B=1, S=T)
+    tgt = args if name in args else kw
+    tgt[name] = meta(*shape, dt=dt)
+    with pytest.raises(ValueError, match=name):
+        m.mla_qup_bwd(args["dq"], args["x"], args["w"], args["dq_pre"], **kw)
+
+
+def test_binding_rejects_bad_quantize_and_kv_tensors(meta):
+    x = meta(8, 64)
+    with pytest.raises(ValueError, match="codes"):
+        m.mxfp8_quantize(x, meta(8, 63, dt=torch.uint8), meta(8, 2, dt=torch.uint8))
+    with pytest.raises(ValueError, match="scales"):
+        m.mxfp8_quantize(x, meta(8, 64, dt=torch.uint8), meta(8, 1, dt=torch.uint8))
+    with pytest.raises(ValueError, match="x is on cpu"):
+        m.mxfp8_quantize(torch.empty(8, 64, dtype=torch.bfloat16), meta(8, 64, dt=torch.uint8),
+                         meta(8, 2, dt=torch.uint8))
+    with pytest.raises(ValueError, match="codes_t"):
+        m.mxfp8_quantize_t(x, meta(64, 16, dt=torch.uint8), meta(64, 1, dt=torch.uint8), rows_pad=32)
+    T, H, dn, dr, dv = 16, 2, 32, 32, 32
+    kv, pe = meta(T, H, dn + dv), meta(T, dr)
+    key, val = meta(1, H, T, dn + dr, dt=torch.uint8), meta(1, H, T, dv, dt=torch.uint8)
+    tab = dict(cos=meta(T, dr // 2, dt=torch.float32), sin=meta(T, dr // 2, dt=torch.float32))
+    with pytest.raises(ValueError, match="value_scales"):
+        m.mla_kv_rope(kv, pe, key, val, H=H, d_nope=dn, d_rope=dr, d_v=dv, key_scales=meta(1, H, T, 2, dt=torch.uint8),
+                      value_scales=meta(1, H, T, 2, dt=torch.uint8), B=1, S=T, **tab)
+    with pytest.raises(ValueError, match="rope_cache_build"):
+        m.rope_cache_build(meta(T, 16, dt=torch.float32), meta(T, 16, dt=torch.float32), 64)

@@ -12,7 +12,8 @@ import torch
 import mla_up_projection_amd as m
 import oracle as o
 from mla_up_projection_amd import synthetic as syn
-from parity import bits16, check_bf16, check_mx, frob_rel, fwd_reference_rows, u8
+from parity import (Guarded, assert_mx_bar, bits16, check_bf16, check_mx, frob_rel, fwd_reference_rows,
+                    merge_stats, mx_stats, parallel_chunks, u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,16 +47,21 @@ def run_fwd(x, w, *, H, dn, dr, out_mx, fmt=m.FMT_BSHD, B=1, S=None, cu=None, ma
     max_pos = max_seqlen if fmt == m.FMT_THD else S
     cos, sin, oc, os_ = rope_tables(rows or max_pos, dr, yarn=yarn)
     shape = o.out_shape(fmt, T, H, D, B, S)
+    # prefilled so unwritten elements show, inside sentinel margins
     if out_mx:
-        out = torch.full(shape, 0x7F, dtype=torch.uint8, device=DEV)
-        sc = torch.full(shape[:3] + (D // 32,), 0xFF, dtype=torch.uint8, device=DEV)
+        go = Guarded(shape, torch.uint8, 0x7F)
+        gs = Guarded(shape[:3] + (D // 32,), torch.uint8, 0xFF)
+        out, sc = go.t, gs.t
     else:
-        out = torch.full(shape, -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)  # NaN
-        sc = None
+        go, gs = Guarded(shape, torch.bfloat16, 0xFF), None   # 0xFFFF: NaN
+        out, sc = go.t, None
     m.mla_qup_fwd(x, w, out, H=H, d_nope=dn, d_rope=dr, cos=cos if dr else None,
                   sin=sin if dr else None, x_scales=x_scales, w_scales=w_scales, bias=bias,
                   out_scales=sc, fmt=fmt, B=B, S=S, cu_seqlens=cu, max_seqlen=max_seqlen)
     torch.cuda.synchronize()
+    go.check("out")
+    if gs is not None:
+        gs.check("out_scales")
     return out, sc, oc, os_
 
 
@@ -286,6 +292,61 @@ def test_fwd_fp8_mfma_mode_accuracy():
     assert rel <= 1e-2
 
 
+def _at_offset(t, offset):
+    """A device copy of t starting `offset` bytes past a 256-byte boundary."""
+    t = t.contiguous()
+    nb = t.numel() * t.element_size()
+    buf = torch.zeros(nb + 512, dtype=torch.uint8, device=DEV)
+    view = buf[offset:offset + nb].view(t.dtype).view(t.shape)
+    view.copy_(t.to(DEV))
+    assert view.data_ptr() % 256 == offset
+    return view
+
+
+def test_fwd_and_bwd_at_minimum_alignment():
+    """Arguments at the smallest alignment the C ABI admits: x, w, out and
+    dq / dq_pre / dx / dw 16 bytes past a 256-byte boundary, the bias 8 bytes
+    past one, cos / sin 16 bytes past one (the widest vector loads the
+    kernels issue on them). Results against the oracle."""
+    T, K, H, dn, dr = 333, 256, 3, 128, 64
+    D, N = dn + dr, H * (dn + dr)
+    x = syn.normal_bf16((T, K), 1.0, 140)
+    w = syn.normal_bf16((N, K), 0.05, 141)
+    bias = syn.normal_bf16((N,), 0.3, 142)
+    cos, sin, oc, os_ = rope_tables(T, dr)
+    c16, s16 = _at_offset(cos, 16), _at_offset(sin, 16)
+    xd, wd, bd_ = _at_offset(x, 16), _at_offset(w, 16), _at_offset(bias, 8)
+    out = _at_offset(torch.zeros(1, H, T, D, dtype=torch.uint8), 16)
+    sc = _at_offset(torch.zeros(1, H, T, D // 32, dtype=torch.uint8), 16)
+    outb = _at_offset(torch.zeros(1, H, T, D, dtype=torch.bfloat16), 16)
+    kw = dict(H=H, d_nope=dn, d_rope=dr, cos=c16, sin=s16, bias=bd_, B=1, S=T)
+    m.mla_qup_fwd(xd, wd, out, out_scales=sc, **kw)
+    m.mla_qup_fwd(xd, wd, outb, **kw)
+    torch.cuda.synchronize()
+    pos, bb, ss = o.token_coords(o.FMT_BSHD, T, 1, T)
+    q64, bound = fwd_reference_rows(x, w, bias, np.arange(T), H=H, d_nope=dn, d_rope=dr, cos=oc,
+                                    sin=os_, pos=pos)
+    check_mx(u8(out)[0].transpose(1, 0, 2), u8(sc)[0].transpose(1, 0, 2), q64, bound, "min-align mx")
+    check_bf16(bits16(outb)[0].transpose(1, 0, 2), o.f32_to_bf16_bits(q64.astype(np.float32)),
+               "min-align bf16")
+    dq = syn.normal_bf16((T, H, D), 1e-3, 143)
+    dqd = _at_offset(dq, 16)
+    dq_pre = _at_offset(torch.zeros(T, N, dtype=torch.bfloat16), 16)
+    dx = _at_offset(torch.zeros(T, K, dtype=torch.bfloat16), 16)
+    dw = _at_offset(torch.zeros(N, K, dtype=torch.bfloat16), 16)
+    db = _at_offset(torch.zeros(N, dtype=torch.bfloat16), 2)
+    bkw = dict(H=H, d_nope=dn, d_rope=dr, cos=c16, sin=s16, dx=dx, dw=dw, db=db, use_bias=True, B=1, S=T)
+    nbytes = m.mla_qup_bwd_workspace_size(dqd, xd, wd, dq_pre, **bkw)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    m.mla_qup_bwd(dqd, xd, wd, dq_pre, workspace=ws if nbytes else None, **bkw)
+    torch.cuda.synchronize()
+    r = o.qup_backward(dq, x, w, H=H, d_nope=dn, d_rope=dr, cos=oc, sin=os_, S=T)
+    check_bf16(bits16(dq_pre), o.f32_to_bf16_bits(r.dq_pre.astype(np.float32)), "min-align dq_pre")
+    assert frob_rel(o.to_f64(dx.cpu()), r.dx) <= 1e-2
+    assert frob_rel(o.to_f64(dw.cpu()), r.dw) <= 1e-2
+    assert frob_rel(o.to_f64(db.cpu()), r.db) <= 1e-2
+
+
 def test_fwd_zero_tokens_enqueues_nothing():
     x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
     w = torch.zeros(64, 64, dtype=torch.bfloat16, device=DEV)
@@ -351,24 +412,34 @@ def run_bwd(dq, x, w, *, H, dn, dr, fmt=m.FMT_BSHD, B=1, S=None, cu=None, max_se
     max_pos = max_seqlen if fmt == m.FMT_THD else S
     cos, sin, oc, os_ = rope_tables(max_pos, dr, yarn=yarn)
     dqd, xd, wd = _dev(dq), _dev(x), _dev(w)
-    dq_pre = torch.empty(T, N, dtype=torch.bfloat16, device=DEV)
-    dx = torch.empty(T, K, dtype=torch.bfloat16, device=DEV) if "dx" in want else None
-    dw = torch.empty(N, K, dtype=torch.float32 if dw_fp32 else torch.bfloat16, device=DEV) \
-        if "dw" in want else None
-    db = torch.empty(N, dtype=torch.bfloat16, device=DEV) if use_bias else None
+    # every output and the workspace inside sentinel margins (out-of-bounds writes)
+    guards = {"dq_pre": Guarded((T, N), torch.bfloat16)}
+    if "dx" in want:
+        guards["dx"] = Guarded((T, K), torch.bfloat16)
+    if "dw" in want:
+        guards["dw"] = Guarded((N, K), torch.float32 if dw_fp32 else torch.bfloat16)
+    if use_bias:
+        guards["db"] = Guarded((N,), torch.bfloat16)
+    out = {k: (guards[k].t if k in guards else None) for k in ("dq_pre", "dx", "dw", "db")}
+    dq_pre = out["dq_pre"]
     kw = dict(H=H, d_nope=dn, d_rope=dr, cos=cos if dr else None, sin=sin if dr else None,
-              dx=dx, dw=dw, db=db, use_bias=use_bias, fmt=fmt, B=B, S=S,
+              dx=out["dx"], dw=out["dw"], db=out["db"], use_bias=use_bias, fmt=fmt, B=B, S=S,
               cu_seqlens=_dev(cu) if cu is not None else None, max_seqlen=max_seqlen)
     if mx is None:
         nbytes = m.mla_qup_bwd_workspace_size(dqd, xd, wd, dq_pre, **kw)
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
-        m.mla_qup_bwd(dqd, xd, wd, dq_pre, workspace=ws if nbytes else None, **kw)
     else:
         nbytes = m.mla_qup_bwd_mxfp8_workspace_size(dqd, xd, wd, dq_pre, **kw)
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
-        m.mla_qup_bwd_mxfp8(dqd, xd, wd, dq_pre, fp8_mfma=mx, workspace=ws if nbytes else None, **kw)
+    if nbytes:
+        guards["workspace"] = Guarded((nbytes,), torch.uint8)
+    ws = guards["workspace"].t if nbytes else None
+    if mx is None:
+        m.mla_qup_bwd(dqd, xd, wd, dq_pre, workspace=ws, **kw)
+    else:
+        m.mla_qup_bwd_mxfp8(dqd, xd, wd, dq_pre, fp8_mfma=mx, workspace=ws, **kw)
     torch.cuda.synchronize()
-    return dict(dq_pre=dq_pre, dx=dx, dw=dw, db=db, oc=oc, os=os_)
+    for k, g in guards.items():
+        g.check(k)
+    return dict(out, oc=oc, os=os_)
 
 
 def test_bwd_small_against_oracle():
@@ -604,32 +675,30 @@ def test_bwd_mxfp8_zero_tokens_zeroes_dw_db():
 
 
 # ------------------------------------------------ full-size named workloads --
-SAMPLE = 96
-
-
-def sample_rows(T, seed=123):
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, 1, T // 2, T - 2, T - 1], rng.integers(0, T, SAMPLE)]))
-    return rows
+# Every output element is compared: the oracle runs over chunks of token rows
+# on a thread pool. Full-size properties are checked too: inputs unchanged,
+# run-to-run bit identity, every output written, no write outside the outputs.
+FULL_CHUNK = 128
 
 
 def _hash(t):
     return hash(t.detach().cpu().contiguous().view(torch.uint8).numpy().tobytes())
 
 
-@pytest.mark.parametrize("name", ["dsv3_fwd_bf16w", "dsv3_fwd_mxfp8w", "thd_yarn_fwd"])
-def test_fwd_full_size_sampled(name):
-    wl = syn.workload(name)
+def _fwd_full_size_run(wl, fp8_mfma=False):
+    """Run one named forward workload at full size (the benchmark's launch
+    configuration), twice, with guarded outputs; returns what the oracle
+    comparison needs."""
     x, w = wl.x(), wl.w()
     T, K = x.shape
     xd, wd = _dev(x), _dev(w)
     cu = wl.cu_seqlens()
     cud = _dev(cu) if cu is not None else None
-    yarn = wl.yarn
     max_pos = wl.max_pos
-    cos, sin, oc, os_ = rope_tables(max_pos, wl.d_rope, yarn=yarn)
+    cos, sin, oc, os_ = rope_tables(max_pos, wl.d_rope, yarn=wl.yarn)
     hx, hw, hc = _hash(xd), _hash(wd), _hash(cos)
     xs = ws = None
+    ref = dict(x=o.to_f64(x), w=o.to_f64(w))
     if wl.mx_weight:
         xq = torch.empty(T, K, dtype=torch.uint8, device=DEV)
         xs = torch.empty(T, K // 32, dtype=torch.uint8, device=DEV)
@@ -638,63 +707,116 @@ def test_fwd_full_size_sampled(name):
         m.mxfp8_quantize(xd, xq, xs)
         m.mxfp8_quantize(wd, wq, ws)
         torch.cuda.synchronize()
-        oxq, oxs = o.mxfp8_quantize_blocks(o.to_f64(x).astype(np.float32))
-        owq, ows = o.mxfp8_quantize_blocks(o.to_f64(w).astype(np.float32))
+        oxq, oxs = o.mxfp8_quantize_blocks(ref["x"].astype(np.float32))
+        owq, ows = o.mxfp8_quantize_blocks(ref["w"].astype(np.float32))
         assert np.array_equal(u8(xs), oxs) and np.array_equal(u8(ws), ows)
         assert np.array_equal(u8(xq), oxq) and np.array_equal(u8(wq), owq)
+        ref = dict(x=o.mxfp8_dequantize(oxq, oxs), w=o.mxfp8_dequantize(owq, ows))
         xin, win = xq, wq
     else:
         xin, win = xd, wd
     shape = o.out_shape(wl.fmt, T, wl.H, wl.D, wl.B, wl.S)
     outs = []
     for rep in range(2):
-        out = torch.full(shape, 0x7F, dtype=torch.uint8, device=DEV)
-        sc = torch.full(shape[:3] + (wl.D // 32,), 0xFF, dtype=torch.uint8, device=DEV)
-        m.mla_qup_fwd(xin, win, out, H=wl.H, d_nope=wl.d_nope, d_rope=wl.d_rope, cos=cos, sin=sin,
-                      x_scales=xs, w_scales=ws, out_scales=sc, fmt=wl.fmt, B=wl.B, S=wl.S,
-                      cu_seqlens=cud, max_seqlen=max_pos)
+        go = Guarded(shape, torch.uint8, 0x7F)
+        gs = Guarded(shape[:3] + (wl.D // 32,), torch.uint8, 0xFF)
+        m.mla_qup_fwd(xin, win, go.t, H=wl.H, d_nope=wl.d_nope, d_rope=wl.d_rope, cos=cos, sin=sin,
+                      x_scales=xs, w_scales=ws, out_scales=gs.t, fmt=wl.fmt, B=wl.B, S=wl.S,
+                      cu_seqlens=cud, max_seqlen=max_pos, fp8_mfma=fp8_mfma)
         torch.cuda.synchronize()
-        outs.append((out, sc))
+        go.check("out")
+        gs.check("out_scales")
+        outs.append((go.t, gs.t))
     # determinism and completeness (finite inputs never give 0xFF scales)
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
     assert not (outs[0][1] == 0xFF).any()
     # inputs untouched, byte for byte
     assert _hash(xd) == hx and _hash(wd) == hw and _hash(cos) == hc
-    out, sc = outs[0]
-    rows = sample_rows(T)
     pos, bb, ss = o.token_coords(wl.fmt, T, wl.B, wl.S, cu.numpy() if cu is not None else None)
-    if wl.mx_weight:
-        q64, bound = fwd_reference_rows(oxq, owq, None, rows, H=wl.H, d_nope=wl.d_nope,
-                                        d_rope=wl.d_rope, cos=oc, sin=os_, pos=pos, x_scales=oxs,
-                                        w_scales=ows)
-    else:
-        q64, bound = fwd_reference_rows(x, w, None, rows, H=wl.H, d_nope=wl.d_nope,
-                                        d_rope=wl.d_rope, cos=oc, sin=os_, pos=pos)
-    bi, si = torch.from_numpy(bb[rows]).to(DEV), torch.from_numpy(ss[rows]).to(DEV)
-    g = out[bi, :, si, :].cpu().numpy()
-    gs = sc[bi, :, si, :].cpu().numpy()
-    stats = check_mx(g, gs, q64, bound, name)
-    print(f"\n{name}: {stats}", flush=True)
+    return dict(out=u8(outs[0][0]), sc=u8(outs[0][1]), ref=ref, oc=oc, os=os_, pos=pos, bb=bb, ss=ss)
 
 
-def test_bwd_full_size_sampled():
+def _fwd_full_size_stats(wl, r):
+    """mx_stats over every token row, in parallel chunks."""
+    xf, wf = r["ref"]["x"], r["ref"]["w"]
+    awf = np.abs(wf)
+
+    def one(lo, hi):
+        rows = np.arange(lo, hi)
+        q64, bound = fwd_reference_rows(xf, wf, None, rows, H=wl.H, d_nope=wl.d_nope, d_rope=wl.d_rope,
+                                        cos=r["oc"], sin=r["os"], pos=r["pos"], abs_w=awf)
+        g = r["out"][r["bb"][rows], :, r["ss"][rows], :]
+        gs = r["sc"][r["bb"][rows], :, r["ss"][rows], :]
+        return mx_stats(g, gs, q64, bound)
+
+    return merge_stats(parallel_chunks(one, xf.shape[0], FULL_CHUNK))
+
+
+@pytest.mark.parametrize("name", ["dsv3_fwd_bf16w", "dsv3_fwd_mxfp8w", "thd_yarn_fwd"])
+def test_fwd_full_size(name):
+    """The three full-size forward workloads (the MXFP8 projection in its
+    default exact mode), every output element against the oracle at the
+    MXFP8 bar."""
+    wl = syn.workload(name)
+    print(f"\n{name}: running", flush=True)
+    r = _fwd_full_size_run(wl)
+    st = assert_mx_bar(_fwd_full_size_stats(wl, r), name)
+    print(f"{name}: {st}", flush=True)
+
+
+def test_fwd_full_size_mxfp8_projection_on_fp8_mfma():
+    """The MXFP8 projection at full size (T = 8192) on the scaled FP8 MFMA,
+    every element against the oracle. The instruction sums each K-step's
+    products in a narrower fixed-point window than float32, so its output is
+    held to its measured deviation, not to the MXFP8 bar: scales and codes
+    are compared, every flip is at most one code step, and the flip and
+    scale-mismatch rates stay within the measured figures."""
+    wl = syn.workload("dsv3_fwd_mxfp8w")
+    print("\ndsv3_fwd_mxfp8w on FP8 MFMA: running", flush=True)
+    r = _fwd_full_size_run(wl, fp8_mfma=True)
+    st = _fwd_full_size_stats(wl, r)
+    flips = st["code_flips"] / st["elements"]
+    smis = (st["scale_adjudicated"] + st["scale_unexplained"]) / st["blocks"]
+    gt1 = st["flip_gt1"] / st["elements"]
+    print(f"dsv3_fwd_mxfp8w fp8_mfma: {st}; code flip fraction {flips:.3e}, more than one step "
+          f"{gt1:.3e}, scale mismatch fraction {smis:.3e}", flush=True)
+    # the measured deviation (deterministic for these seeded inputs), with a
+    # margin for a reordered reduction
+    assert flips <= 1.2e-3, flips
+    assert gt1 <= 6e-5, gt1
+    assert smis <= 1.2e-5 and st["scale_unexplained"] == 0, st
+    assert st["flip_unexplained"] == 0, st
+
+
+def test_bwd_full_size():
+    """DeepSeek-V3 backward at full size, every element: dq_pre by the BF16
+    rule, dX, dW and db by relative Frobenius error, with guarded outputs."""
     wl = syn.workload("dsv3_bwd")
     x, w, dq = wl.x(), wl.w(), wl.dq()
     T, K, N = wl.T, wl.K, wl.N
+    print("\ndsv3_bwd: running", flush=True)
     g = run_bwd(dq, x, w, H=wl.H, dn=wl.d_nope, dr=wl.d_rope, S=wl.S, use_bias=True)
     pos, _, _ = o.token_coords(o.FMT_BSHD, T, 1, T)
-    dq64 = o.to_f64(dq)
-    dq_pre = o.rope_rotate(dq64, pos, g["oc"], g["os"], wl.d_nope, wl.d_rope, inverse=True).reshape(T, N)
-    rows = sample_rows(T)
-    check_bf16(bits16(g["dq_pre"][torch.from_numpy(rows).to(DEV)]),
-               o.f32_to_bf16_bits(dq_pre[rows].astype(np.float32)), "dq_pre")
+    dq_pre = o.rope_rotate(o.to_f64(dq), pos, g["oc"], g["os"], wl.d_nope, wl.d_rope, inverse=True).reshape(T, N)
+    gq = bits16(g["dq_pre"])
+    st = parallel_chunks(lambda lo, hi: check_bf16(gq[lo:hi], o.f32_to_bf16_bits(dq_pre[lo:hi].astype(np.float32)),
+                                                   "dq_pre"), T, 256)
+    print(f"dq_pre worst max_rel {max(c['max_rel'] for c in st):.3e}", flush=True)
     wf, xf = o.to_f64(w), o.to_f64(x)
-    dx_ref = dq_pre[rows] @ wf
-    assert frob_rel(o.to_f64(g["dx"][torch.from_numpy(rows).to(DEV)].cpu()), dx_ref) <= 1e-2
-    nrows = sample_rows(N, seed=7)
-    dw_ref = dq_pre[:, nrows].T @ xf
-    assert frob_rel(o.to_f64(g["dw"][torch.from_numpy(nrows).to(DEV)].cpu()), dw_ref) <= 1e-2
-    assert frob_rel(o.to_f64(g["db"].cpu()), dq_pre.sum(0)) <= 1e-2
+    ex = frob_rel(o.to_f64(g["dx"].cpu()), dq_pre @ wf)
+    ew = frob_rel(o.to_f64(g["dw"].cpu()), dq_pre.T @ xf)
+    eb = frob_rel(o.to_f64(g["db"].cpu()), dq_pre.sum(0))
+    print(f"dsv3_bwd: dx {ex:.2e} dw {ew:.2e} db {eb:.2e}", flush=True)
+    assert ex <= 1e-2 and ew <= 1e-2 and eb <= 1e-2
+
+
+SAMPLE = 96
+
+
+def sample_rows(T, seed=123):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, T // 2, T - 2, T - 1], rng.integers(0, T, SAMPLE)]))
+    return rows
 
 
 def test_bwd_tp8_shard_sampled():
