@@ -61,7 +61,9 @@ enum {
   MLA_EALIAS = 3,        /* an output overlaps an input, output or workspace */
   MLA_EUNSUPPORTED = 4,  /* valid combination this library does not implement */
   MLA_EDEVICE = 5,       /* the HIP runtime reported an error at launch */
-  MLA_EWORKSPACE = 6     /* workspace NULL or smaller than required */
+  MLA_EWORKSPACE = 6,    /* workspace NULL or smaller than required */
+  MLA_ESCRATCH = 7       /* mla_qup_bwd_noalloc: the call needs more than the
+                            library's static scratch (MLA_BWD_SCRATCH_BYTES) */
 };
 
 enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1, MLA_DTYPE_MXFP8 = 2 };
@@ -259,6 +261,23 @@ MLA_API size_t mla_qup_bwd_workspace_size(const mla_qup_bwd_args* args);
  * Errors: MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EWORKSPACE,
  * MLA_EDEVICE. */
 MLA_API mla_status mla_qup_bwd(const mla_qup_bwd_args* args, void* stream);
+
+/* Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, results and errors as mla_qup_bwd, except that
+ * `workspace` and `workspace_bytes` are ignored: the partial sums live in a
+ * static device array of MLA_BWD_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends (looked up once per device, with the
+ * stream's device current). When the workspace plan of mla_qup_bwd does not
+ * fit, dX and dW are computed without reduction splits (no split partials);
+ * if the db partials alone (ceil(T/64) * N * 4 bytes at most) still do not
+ * fit: MLA_ESCRATCH. Calls that overlap on one GPU (several streams or host
+ * threads) race on that one array: serialize them. The array keeps the last
+ * call's contents; nothing in it needs to start at zero. Allocates nothing.
+ * Errors: as mla_qup_bwd (never MLA_EWORKSPACE), plus MLA_ESCRATCH, and
+ * MLA_EINVAL when the stream belongs to a device other than the current one. */
+#define MLA_BWD_SCRATCH_BYTES ((size_t)64 << 20)
+MLA_API mla_status mla_qup_bwd_noalloc(const mla_qup_bwd_args* args, void* stream);
 
 /* MXFP8 backward: the forward page's "mxfp8 projection" carried into the
  * backward page's linear backward. Same arguments, outputs and dq_pre / db

@@ -5,5 +5,5 @@ in include/mla_qup.h); `binding` marshals torch device tensors into it.
 """
 from .binding import (  # noqa: F401
     DTYPE_BF16, DTYPE_FP32, DTYPE_MXFP8, FMT_BSHD, FMT_SBHD, FMT_THD, FUNCTIONS, LIB_PATH, MlaError,
-    lib, mla_qup_bwd, mla_qup_bwd_mxfp8, mla_qup_bwd_mxfp8_workspace_size, mla_qup_bwd_workspace_size,
+    lib, mla_qup_bwd, mla_qup_bwd_mxfp8, mla_qup_bwd_noalloc, mla_qup_bwd_mxfp8_workspace_size, mla_qup_bwd_workspace_size,
     mla_kv_rope, mla_qup_fwd, mla_status_str, mxfp8_quantize, mxfp8_quantize_t, rope_cache_build)

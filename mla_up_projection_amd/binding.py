@@ -17,13 +17,15 @@ import torch  # imported before the library so both share torch's HIP runtime
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmlaqup.so")
 
 MLA_FWD_FP8_MFMA = 1
-MLA_OK, MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EUNSUPPORTED, MLA_EDEVICE, MLA_EWORKSPACE = range(7)
+(MLA_OK, MLA_EINVAL, MLA_EROPE_TABLE, MLA_EALIAS, MLA_EUNSUPPORTED, MLA_EDEVICE, MLA_EWORKSPACE,
+ MLA_ESCRATCH) = range(8)
+MLA_BWD_SCRATCH_BYTES = 64 << 20
 DTYPE_BF16, DTYPE_FP32, DTYPE_MXFP8 = 0, 1, 2
 FMT_BSHD, FMT_SBHD, FMT_THD = 0, 1, 2
 
 FUNCTIONS = ("rope_cache_build", "mxfp8_quantize", "mxfp8_quantize_t", "mla_qup_fwd", "mla_qup_bwd",
-             "mla_qup_bwd_workspace_size", "mla_qup_bwd_mxfp8", "mla_qup_bwd_mxfp8_workspace_size",
-             "mla_kv_rope", "mla_status_str")
+             "mla_qup_bwd_workspace_size", "mla_qup_bwd_noalloc", "mla_qup_bwd_mxfp8",
+             "mla_qup_bwd_mxfp8_workspace_size", "mla_kv_rope", "mla_status_str")
 
 
 class mla_tokens(Structure):
@@ -86,6 +88,7 @@ def lib() -> ctypes.CDLL:
         L.mla_qup_bwd.argtypes = [POINTER(mla_qup_bwd_args), c_void_p]
         L.mla_qup_bwd_workspace_size.argtypes = [POINTER(mla_qup_bwd_args)]
         L.mla_qup_bwd_workspace_size.restype = c_size_t
+        L.mla_qup_bwd_noalloc.argtypes = [POINTER(mla_qup_bwd_args), c_void_p]
         L.mla_qup_bwd_mxfp8.argtypes = [POINTER(mla_qup_bwd_args), c_int32, c_void_p]
         L.mla_qup_bwd_mxfp8_workspace_size.argtypes = [POINTER(mla_qup_bwd_args)]
         L.mla_qup_bwd_mxfp8_workspace_size.restype = c_size_t
@@ -93,7 +96,7 @@ def lib() -> ctypes.CDLL:
         L.mla_status_str.argtypes = [c_int32]
         L.mla_status_str.restype = c_char_p
         for f in ("rope_cache_build", "mxfp8_quantize", "mxfp8_quantize_t", "mla_qup_fwd", "mla_qup_bwd",
-                  "mla_qup_bwd_mxfp8", "mla_kv_rope"):
+                  "mla_qup_bwd_noalloc", "mla_qup_bwd_mxfp8", "mla_kv_rope"):
             getattr(L, f).restype = c_int32
         _lib = L
     return _lib
@@ -318,6 +321,16 @@ def mla_qup_bwd(dq, x, w, dq_pre, *, stream=None, **kw):
     mla_qup_bwd_workspace_size() bytes (None if that is 0)."""
     a = make_bwd_args(dq, x, w, dq_pre, **kw)
     _check(lib().mla_qup_bwd(ctypes.byref(a), _stream(stream)), "mla_qup_bwd")
+
+
+def mla_qup_bwd_noalloc(dq, x, w, dq_pre, *, stream=None, **kw):
+    """Backward as mla_qup_bwd, with the partial sums in the library's static
+    scratch instead of a workspace (nothing is allocated; calls that overlap on
+    one GPU race on that scratch). No workspace argument."""
+    if kw.get("workspace") is not None:
+        raise ValueError("mla_qup_bwd_noalloc takes no workspace")
+    a = make_bwd_args(dq, x, w, dq_pre, **kw)
+    _check(lib().mla_qup_bwd_noalloc(ctypes.byref(a), _stream(stream)), "mla_qup_bwd_noalloc")
 
 
 def mla_qup_bwd_mxfp8_workspace_size(dq, x, w, dq_pre, **kw) -> int:

@@ -7,9 +7,17 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "internal.h"
+
+// Scratch memory of mla_qup_bwd_noalloc: one copy per GPU in this code
+// object's static device data, held until the process ends. In host code the
+// name `scratch` is only a stand-in for the device symbol (using it as an
+// address would fault on the GPU); each GPU's copy is reached through the
+// address hipGetSymbolAddress returns for it (scratch_for_current_device).
+static __device__ __align__(256) uint8_t scratch[MLA_BWD_SCRATCH_BYTES];
 
 namespace {
 
@@ -88,6 +96,25 @@ size_t rope_bytes(const mla_rope& r, int32_t d_rope) {
   return d_rope ? (size_t)r.rows * (size_t)r.pairs * sizeof(float) : 0;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current, and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+mla_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MLA_EDEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
 void fill_token_map(const mla_tokens& tk, int& fmt, int& B, int& S, const int32_t*& cu, int& nseq) {
   fmt = tk.fmt;
   if (tk.fmt == MLA_FMT_THD) {
@@ -131,6 +158,9 @@ const char* mla_status_str(mla_status s) {
     case MLA_EUNSUPPORTED: return "MLA_EUNSUPPORTED: unsupported combination";
     case MLA_EDEVICE: return "MLA_EDEVICE: HIP launch error";
     case MLA_EWORKSPACE: return "MLA_EWORKSPACE: workspace missing or too small";
+    case MLA_ESCRATCH:
+      return "MLA_ESCRATCH: the backward needs more scratch than mla_qup_bwd_noalloc's static "
+             "array (MLA_BWD_SCRATCH_BYTES) holds; use mla_qup_bwd with a workspace";
     default: return "unknown mla_status";
   }
 }
@@ -353,16 +383,22 @@ size_t mla_qup_bwd_mxfp8_workspace_size(const mla_qup_bwd_args* a) {
   return mla::plan_bwd_mx(a->tokens.T, N, a->K, a->use_bias != 0).total;
 }
 
-static mla_status qup_bwd_impl(const mla_qup_bwd_args* a, int mx, int fp8_mfma, void* stream);
+static mla_status qup_bwd_impl(const mla_qup_bwd_args* a, int mx, int fp8_mfma, bool noalloc, void* stream);
 
-mla_status mla_qup_bwd(const mla_qup_bwd_args* a, void* stream) { return qup_bwd_impl(a, 0, 0, stream); }
+mla_status mla_qup_bwd(const mla_qup_bwd_args* a, void* stream) { return qup_bwd_impl(a, 0, 0, false, stream); }
+
+mla_status mla_qup_bwd_noalloc(const mla_qup_bwd_args* a, void* stream) {
+  return qup_bwd_impl(a, 0, 0, true, stream);
+}
 
 mla_status mla_qup_bwd_mxfp8(const mla_qup_bwd_args* a, int32_t fp8_mfma, void* stream) {
   if (fp8_mfma != 0 && fp8_mfma != 1) return MLA_EINVAL;
-  return qup_bwd_impl(a, 1, fp8_mfma, stream);
+  return qup_bwd_impl(a, 1, fp8_mfma, false, stream);
 }
 
-static mla_status qup_bwd_impl(const mla_qup_bwd_args* a, int mx, int fp8_mfma, void* stream) {
+// noalloc: the partial sums go to the library's static scratch instead of the
+// caller's workspace (mla_qup_bwd_noalloc; bf16 backward only).
+static mla_status qup_bwd_impl(const mla_qup_bwd_args* a, int mx, int fp8_mfma, bool noalloc, void* stream) {
   int64_t max_pos = 0;
   mla_status st = check_bwd_shapes(a, &max_pos);
   if (st) return st;
@@ -385,7 +421,11 @@ static mla_status qup_bwd_impl(const mla_qup_bwd_args* a, int mx, int fp8_mfma, 
     plan = mplan.base;
     plan.total = mplan.total;
   }
-  if (plan.total > 0) {
+  if (noalloc) {
+    if (plan.total > MLA_BWD_SCRATCH_BYTES)  // fall back to unsplit reductions (no split partials)
+      plan = mla::plan_bwd(T, N, a->K, a->use_bias != 0, a->dx != nullptr, a->dw != nullptr, false);
+    if (plan.total > MLA_BWD_SCRATCH_BYTES) return MLA_ESCRATCH;
+  } else if (plan.total > 0) {
     if (a->workspace == nullptr || a->workspace_bytes < plan.total) return MLA_EWORKSPACE;
     if (!aligned(a->workspace, 256)) return MLA_EINVAL;
   }
@@ -401,8 +441,20 @@ static mla_status qup_bwd_impl(const mla_qup_bwd_args* a, int mx, int fp8_mfma, 
   if (a->dx) outs.push_back(rng(a->dx, (size_t)T * a->K * 2));
   if (a->dw) outs.push_back(rng(a->dw, (size_t)N * a->K * (a->dw_dtype == MLA_DTYPE_FP32 ? 4 : 2)));
   if (a->use_bias) outs.push_back(rng(a->db, (size_t)N * 2));
-  if (plan.total) outs.push_back(rng(a->workspace, plan.total));
+  if (plan.total && !noalloc) outs.push_back(rng(a->workspace, plan.total));
   if (overlaps(outs, ins)) return MLA_EALIAS;
+  void* workspace = a->workspace;
+  if (noalloc) {
+    // the scratch of the device the stream runs on, which must be current
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return MLA_EDEVICE;
+    if (stream != nullptr) {
+      if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return MLA_EDEVICE;
+      if (sdev != cur) return MLA_EINVAL;
+    }
+    mla_status sst = scratch_for_current_device(&workspace);
+    if (sst) return sst;
+  }
 
   mla::BwdParams p{};
   p.dq = (const uint16_t*)a->dq;
@@ -426,7 +478,7 @@ static mla_status qup_bwd_impl(const mla_qup_bwd_args* a, int mx, int fp8_mfma, 
   p.dw_fp32 = a->dw_dtype == MLA_DTYPE_FP32;
   p.use_bias = a->use_bias;
   p.db = (uint16_t*)a->db;
-  p.workspace = a->workspace;
+  p.workspace = workspace;
   if (mx) return launched(mla::launch_qup_bwd_mx(p, mplan, fp8_mfma, (hipStream_t)stream));
   return launched(mla::launch_qup_bwd(p, plan, (hipStream_t)stream));
 }

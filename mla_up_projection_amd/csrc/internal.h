@@ -90,7 +90,9 @@ struct MxBwdPlan {
   size_t dx_part;
   size_t total;
 };
-BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx, bool want_dw);
+// allow_splits = false plans dX and dW without reduction splits (no split
+// partials: the smallest workspace).
+BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx, bool want_dw, bool allow_splits = true);
 // Reduction values per stage of the dX product (64, or 32 when N % 64 != 0).
 int dx_stage_depth(int N);
 

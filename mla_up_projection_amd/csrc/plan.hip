@@ -69,7 +69,7 @@ static int dw_split_count(int64_t T, int N, int K) {
   return (int)((stages + sps - 1) / sps);  // no empty split
 }
 
-BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx, bool want_dw) {
+BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx, bool want_dw, bool allow_splits) {
   BwdPlan pl{};
   // Rows per inverse-RoPE workgroup: the most (up to 64) that still give
   // 1536 workgroups, the count that runs at copy speed at DeepSeek-V3 shape
@@ -84,10 +84,10 @@ BwdPlan plan_bwd(int64_t T, int N, int K, bool use_bias, bool want_dx, bool want
   pl.db_row_chunks = (int)((T + pl.ir_rows - 1) / pl.ir_rows);
   pl.db_off = 0;
   pl.db_bytes = use_bias ? align256((size_t)pl.db_row_chunks * N * 4) : 0;
-  pl.dx_splits = want_dx && T > 0 ? dx_split_count(T, N, K) : 1;
+  pl.dx_splits = want_dx && T > 0 && allow_splits ? dx_split_count(T, N, K) : 1;
   pl.dx_off = pl.db_bytes;
   pl.dx_bytes = pl.dx_splits > 1 ? align256((size_t)pl.dx_splits * T * K * 4) : 0;
-  pl.dw_splits = want_dw && T > 0 ? dw_split_count(T, N, K) : 1;
+  pl.dw_splits = want_dw && T > 0 && allow_splits ? dw_split_count(T, N, K) : 1;
   pl.dw_off = pl.dx_off + pl.dx_bytes;
   pl.dw_bytes = pl.dw_splits > 1 ? align256((size_t)pl.dw_splits * N * K * 4) : 0;
   pl.total = pl.db_bytes + pl.dx_bytes + pl.dw_bytes;

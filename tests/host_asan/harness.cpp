@@ -29,6 +29,8 @@ hipError_t launch_qup_bwd_mx(const BwdParams&, const MxBwdPlan&, int, hipStream_
 }  // namespace mla
 hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
 hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t, int) { *v = 256; return hipSuccess; }
+hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* d) { *d = 0; return hipSuccess; }
+hipError_t hipGetSymbolAddress(void** p, const void* sym) { *p = const_cast<void*>(sym); return hipSuccess; }
 
 // ---- driver ----
 static int g_fail = 0;
@@ -130,6 +132,16 @@ int main() {
     }
   }
   b = bwd0(); b.tokens.T = 0; b.tokens.S = 0; EXPECT(mla_qup_bwd(&b, nullptr), MLA_EINVAL);
+  // allocation-free backward: the workspace arguments are ignored; a plan that
+  // does not fit the static scratch falls back to unsplit reductions, and only
+  // db partials beyond it are refused
+  b = bwd0(); b.workspace = nullptr; b.workspace_bytes = 0;
+  EXPECT(mla_qup_bwd_noalloc(&b, nullptr), MLA_OK);
+  EXPECT(mla_qup_bwd_noalloc(&b, (void*)0x1234), MLA_OK);  // stub: stream on device 0
+  b.tokens.T = 1 << 20; b.tokens.S = 1 << 20; b.rope.rows = 1 << 20;  // db partials 16384 x N x 4 B
+  EXPECT(mla_qup_bwd_noalloc(&b, nullptr), MLA_ESCRATCH);
+  b.use_bias = 0; b.db = nullptr; EXPECT(mla_qup_bwd_noalloc(&b, nullptr), MLA_OK);  // unsplit: no partials
+  b = bwd0(); b.dq_pre = nullptr; EXPECT(mla_qup_bwd_noalloc(&b, nullptr), MLA_EINVAL);
   // KV side
   mla_kv_args k = kv0();
   EXPECT(mla_kv_rope(&k, nullptr), MLA_OK);

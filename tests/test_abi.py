@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(7):
+    for code in range(8):
         assert m.mla_status_str(code).startswith("MLA_")
     assert "unknown" in m.mla_status_str(99)
 
@@ -218,6 +218,21 @@ def test_bwd_workspace_db_bands(L):
 ])
 def test_bwd_validation(L, over, code):
     assert L.mla_qup_bwd(ctypes.byref(bwd_args(**over)), None) == code
+
+
+def test_bwd_noalloc_validation(L):
+    """The allocation-free backward validates like mla_qup_bwd (its workspace
+    arguments are ignored) and refuses, with its own status, a call whose db
+    partials exceed the static scratch."""
+    nows = dict(workspace=0, workspace_bytes=0)
+    assert L.mla_qup_bwd_noalloc(ctypes.byref(bwd_args(**nows, db=0)), None) == bd.MLA_EINVAL
+    assert L.mla_qup_bwd_noalloc(ctypes.byref(bwd_args(**nows, rope__pairs=16)), None) == bd.MLA_EROPE_TABLE
+    assert L.mla_qup_bwd_noalloc(ctypes.byref(bwd_args(**nows, dx=addr(1, 512))), None) == bd.MLA_EALIAS
+    # 2^20 tokens x 768 columns: db partials of 16384 bands x 768 x 4 B = 48 MiB fit;
+    # 128 heads (N = 24576): 1.5 GiB do not
+    big = dict(nows, tokens__T=1 << 20, tokens__S=1 << 20, rope__rows=1 << 20, H=128)
+    assert L.mla_qup_bwd_noalloc(ctypes.byref(bwd_args(**big)), None) == bd.MLA_ESCRATCH
+    assert "MLA_BWD_SCRATCH_BYTES" in m.mla_status_str(bd.MLA_ESCRATCH)
 
 
 def test_bwd_mxfp8_workspace_and_validation(L):
