@@ -15,36 +15,64 @@
 namespace mla {
 namespace {
 
-template <bool FP32>
-__global__ __launch_bounds__(256) void mxfp8_quant_kernel(const void* __restrict__ x, int64_t rows,
-                                                          int64_t cols, int64_t ld,
+// Work split of the row quantization: a workgroup takes MQ_U * 256
+// consecutive groups of 8 elements; thread i handles groups i, i + 256, ...
+// (each of those is one coalesced 1-4 KB wave load), and issues all its loads
+// before any arithmetic, so MQ_U 16-byte loads per lane are in flight.
+// Codes are [rows, cols] and scales [rows, cols/32] row-major with no row
+// padding, so group g's codes start at byte 8 g and its scale is byte g / 4;
+// only a row-strided x (ld != cols) needs g's row, found with 32-bit
+// division when the group count allows it.
+constexpr int MQ_U = 4;
+
+template <bool FP32, bool DENSE, bool IDX32>
+__global__ __launch_bounds__(256) void mxfp8_quant_kernel(const void* __restrict__ x, int64_t groups,
+                                                          int64_t gpr, int64_t ld,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
-  const int64_t groups = rows * (cols / 8);
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
-    const int64_t e = g * 8;
-    const int64_t row = e / cols;
-    const int64_t col = e - row * cols;
+  constexpr int EB = FP32 ? 4 : 2;  // bytes per input element
+  const int64_t g0 = (int64_t)blockIdx.x * (256 * MQ_U) + threadIdx.x;
+  u32x4_t raw[MQ_U][FP32 ? 2 : 1];
+#pragma unroll
+  for (int u = 0; u < MQ_U; ++u) {
+    int64_t g = g0 + 256 * u;
+    if (g >= groups) g = groups - 1;  // recomputes a valid group; stored only if live
+    int64_t e;  // element offset of the group in x
+    if (DENSE) {
+      e = g * 8;
+    } else if (IDX32) {
+      const uint32_t row = (uint32_t)g / (uint32_t)gpr;
+      e = (int64_t)row * ld + (int64_t)((uint32_t)g - row * (uint32_t)gpr) * 8;
+    } else {
+      const int64_t row = g / gpr;
+      e = row * ld + (g - row * gpr) * 8;
+    }
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(x) + e * EB);
+    raw[u][0] = __builtin_nontemporal_load(src);  // x is read exactly once
+    if (FP32) raw[u][FP32 ? 1 : 0] = __builtin_nontemporal_load(src + 1);
+  }
+#pragma unroll
+  for (int u = 0; u < MQ_U; ++u) {
+    const int64_t g = g0 + 256 * u;
     float v[8];
     if (FP32) {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + row * ld + col);
-      const float4 a = p[0], b = p[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-      const uint4 u =
-          *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + row * ld + col);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-        v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+        v[i] = __uint_as_float(raw[u][0][i]);
+        v[4 + i] = __uint_as_float(raw[u][FP32 ? 1 : 0][i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_bits_to_f32(raw[u][0][i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_bits_to_f32(raw[u][0][i] >> 16);
       }
     }
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = max(m, abs_bits(v[i]));
+    // the four lanes of a 32-element block are consecutive (groups are
+    // 32-aligned in a row and rows hold whole blocks)
     m = max(m, (uint32_t)__shfl_xor((int)m, 1));
     m = max(m, (uint32_t)__shfl_xor((int)m, 2));
     uint32_t c0 = 0, c1 = 0, sc;
@@ -57,8 +85,10 @@ __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const void* __restrict
       c1 = e4m3_pack4(v[4], v[5], v[6], v[7], E);
       sc = (uint32_t)(E + 127);
     }
-    *reinterpret_cast<uint2*>(codes + row * cols + col) = make_uint2(c0, c1);
-    if ((g & 3) == 0) scales[row * (cols / 32) + col / 32] = (uint8_t)sc;
+    if (g < groups) {
+      *reinterpret_cast<uint2*>(codes + g * 8) = make_uint2(c0, c1);
+      if ((g & 3) == 0) scales[g >> 2] = (uint8_t)sc;
+    }
   }
 }
 
@@ -131,15 +161,22 @@ hipError_t launch_mxfp8_quantize_t(const void* x, int64_t rows, int64_t cols, in
 
 hipError_t launch_mxfp8_quantize(const void* x, int x_fp32, int64_t rows, int64_t cols, int64_t ld,
                                  uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-  const int64_t groups = rows * (cols / 8);
-  int64_t blocks = (groups + 255) / 256;
-  if (blocks > 16384) blocks = 16384;
-  if (x_fp32)
-    hipLaunchKernelGGL(mxfp8_quant_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
-                       rows, cols, ld, codes, scales);
-  else
-    hipLaunchKernelGGL(mxfp8_quant_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
-                       rows, cols, ld, codes, scales);
+  const int64_t gpr = cols / 8;
+  const int64_t groups = rows * gpr;
+  const dim3 grid((unsigned)((groups + 256 * MQ_U - 1) / (256 * MQ_U)));
+  const bool dense = ld == cols, idx32 = groups < ((int64_t)1 << 32);
+#define MQ_LAUNCH(F, D, I) \
+  hipLaunchKernelGGL((mxfp8_quant_kernel<F, D, I>), grid, dim3(256), 0, stream, x, groups, gpr, ld, codes, scales)
+  if (x_fp32) {
+    if (dense) MQ_LAUNCH(true, true, true);
+    else if (idx32) MQ_LAUNCH(true, false, true);
+    else MQ_LAUNCH(true, false, false);
+  } else {
+    if (dense) MQ_LAUNCH(false, true, true);
+    else if (idx32) MQ_LAUNCH(false, false, true);
+    else MQ_LAUNCH(false, false, false);
+  }
+#undef MQ_LAUNCH
   return hipGetLastError();
 }
 
