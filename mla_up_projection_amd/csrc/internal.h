@@ -15,6 +15,9 @@ constexpr int FWD_TILE_N = 192;           // forward tile: rows of N
 constexpr int IR_THREADS = 128;           // inverse-RoPE workgroup
 constexpr int IR_COLS = IR_THREADS * 8;   // its columns
 constexpr int IR_ROWS = 64;               // its token rows, at most
+// Token rows per band of the MXFP8 backward's fused pass over dq (db
+// partials: one row per band).
+constexpr int MX_BAND_ROWS = 128;
 constexpr int BG_TI = 192;                // backward GEMM tile: output columns
 constexpr int BG_TJ = 128;                // backward GEMM tile: output rows
 constexpr int BG_WG_PER_CU = 2;           // backward GEMM workgroups per CU

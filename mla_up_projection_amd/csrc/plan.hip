@@ -118,6 +118,12 @@ static int mx_split_count(int64_t tiles, int64_t stages) {
 MxBwdPlan plan_bwd_mx(int64_t T, int N, int K, bool use_bias) {
   MxBwdPlan pl{};
   pl.base = plan_bwd(T, N, K, use_bias, false, false);
+  // the fused pass over dq takes bands of MX_BAND_ROWS rows: one db partial
+  // row per band
+  pl.base.ir_rows = MX_BAND_ROWS;
+  pl.base.db_row_chunks = (int)((T + MX_BAND_ROWS - 1) / MX_BAND_ROWS);
+  pl.base.db_bytes = use_bias ? align256((size_t)pl.base.db_row_chunks * N * 4) : 0;
+  pl.base.total = pl.base.db_bytes;
   pl.Tp = (T + 127) / 128 * 128;
   size_t off = pl.base.total;
   auto take = [&](size_t bytes) {

@@ -36,6 +36,16 @@ namespace {
 // IR_THREADS, IR_COLS (columns per workgroup) and IR_ROWS (token rows per
 // workgroup, at most) are shared with the host planner (internal.h).
 
+// Inverse rotation of one (even, odd) pair by the angle whose cosine and sine
+// are c and s, with its fused multiply-adds written out so that every kernel
+// applying it rounds alike.
+__device__ __forceinline__ void inv_rotate(float& a, float& b, float c, float s) {
+  const float na = fmaf(a, c, b * s);
+  const float nb = fmaf(b, c, -(a * s));
+  a = na;
+  b = nb;
+}
+
 // RQ: also quantize each dq_pre row along n from its bf16 copy (the MXFP8
 // backward's dX operand): the four lanes of a 32-column block share its amax
 // through two xor-shuffles; codes [T, N] and scales [T, N/32].
@@ -113,13 +123,7 @@ __global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, int b
       for (int k = 0; k < 4; ++k) {
         float a = bf16_bits_to_f32(g[j][k] & 0xFFFFu);
         float b = bf16_bits_to_f32(g[j][k] >> 16);
-        if (any_rot && rot[k]) {
-          const float c = cs[j][k], s = sn[j][k];
-          const float na = a * c + b * s;
-          const float nb = b * c - a * s;
-          a = na;
-          b = nb;
-        }
+        if (any_rot && rot[k]) inv_rotate(a, b, cs[j][k], sn[j][k]);
         sum[2 * k] += a;
         sum[2 * k + 1] += b;
         o[k] = pack_bf16x2(a, b);
@@ -158,6 +162,243 @@ __global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, int b
     reinterpret_cast<float4*>(dst)[0] = make_float4(sum[0], sum[1], sum[2], sum[3]);
     reinterpret_cast<float4*>(dst)[1] = make_float4(sum[4], sum[5], sum[6], sum[7]);
   }
+}
+
+// MXFP8 backward's pass over dq, fused: inverse RoPE into dq_pre (bf16),
+// dq_pre quantized along n (the dX operand, [T, N] codes + [T, N/32]
+// scales), dq_pre quantized along the tokens and stored transposed (the dW
+// operand, [N, Tp] codes + [N, Tp/32] scales, rows past T as zeros), and the
+// db partial sums of each 128-row band. One read of dq instead of a second
+// pass that reads dq_pre back for the quantization along the tokens.
+// Workgroup tile: 128 token rows (four 32-row blocks) x 128 columns, kept in
+// LDS as bf16 between the two phases (row pitch 256 B). N is a multiple of
+// 128, so every tile is whole along n.
+//   Phase 1: thread t takes 8-column chunk t % 16 of rows t / 16 + 16 i
+//     (i < 8); the eight 16-byte dq loads and their cos/sin entries are all
+//     issued before any arithmetic. Rotates, stores dq_pre, quantizes along n
+//     (the four lanes of a 32-column block share its amax through two quad
+//     DPP moves); rows past T are zeros in LDS and stored nowhere.
+//   Phase 2: wave w takes row block w; lane l the columns 2 l and 2 l + 1:
+//     32 four-byte LDS reads down the column pair (one wave reads a 256-byte
+//     row per step), one amax per column, 32 codes per column stored as 32
+//     contiguous bytes; the four waves write each column's 128 bytes.
+// db: each thread sums its 8 rows of its 8 columns in row order; the 16 row
+// groups are added in a fixed tree (the four of a wave by xor-shuffles, then
+// the four waves in order), so the partial sums are deterministic.
+// Bands whose 128 rows are all tokens take a path with no per-row checks.
+constexpr int MXB_ROWS = 128;
+constexpr int MXB_COLS = 128;
+static_assert(MXB_ROWS == MX_BAND_ROWS, "the planner sizes the db partials by this band");
+
+// Largest value of m over the four lanes of an aligned quad (DPP quad
+// permutations: lanes xor 1, then xor 2).
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, true));
+  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, true));
+  return m;
+}
+
+// Float32 bit pattern of the largest |x| over the 2 k bf16 values packed in
+// w[0 .. k-1] (low halves and high halves maxed apart, as integers).
+template <int K>
+__device__ __forceinline__ uint32_t packed_bf16_amax(const uint32_t* w) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    lo = max(lo, w[i] & 0x7FFFu);
+    hi = max(hi, w[i] & 0x7FFF0000u);
+  }
+  return max(lo << 16, hi);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <bool FULL>
+__device__ __forceinline__ void mx_pass_band(const BwdParams& p, int64_t Tp, int64_t band, int rows, int nt0,
+                                             float* __restrict__ db_part, uint8_t* __restrict__ rc,
+                                             uint8_t* __restrict__ rs, uint8_t* __restrict__ tc,
+                                             uint8_t* __restrict__ ts, uint32_t* tile, float (*red)[MXB_COLS],
+                                             const int* s_pos) {
+  const int tid = threadIdx.x;
+  const int64_t r0 = band * MXB_ROWS;
+
+  // ---- phase 1 ----
+  const int chunk = tid & 15, rg = tid >> 4;
+  const int n0 = nt0 + 8 * chunk;
+  const int d0 = n0 % p.D;  // 8 consecutive columns stay inside one head
+  bool rot[4];
+  int pi[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int d = d0 + 2 * k;
+    rot[k] = p.d_rope > 0 && d >= p.d_nope;
+    pi[k] = rot[k] ? (d - p.d_nope) >> 1 : 0;
+  }
+  const bool any_rot = rot[0] || rot[1] || rot[2] || rot[3];
+  const bool vec4 = rot[0] && rot[3] && (pi[0] & 3) == 0 && (p.rope_pairs & 3) == 0;
+  const int64_t step = (int64_t)16 * p.N;  // elements between a thread's rows
+  const uint16_t* src = p.dq + (r0 + rg) * p.N + n0;
+  u32x4_t g[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (FULL || rg + 16 * i < rows)
+      g[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + i * step));
+    else
+      g[i] = u32x4_t{0, 0, 0, 0};
+  }
+  float cs[8][4], sn[8][4];
+  if (any_rot) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pos = s_pos[rg + 16 * i];  // -1: beyond the table; pad rows hold 0
+      if (pos >= 0) {
+        const float* ct = p.cos + (int64_t)pos * p.rope_pairs;
+        const float* st = p.sin + (int64_t)pos * p.rope_pairs;
+        if (vec4) {
+          const float4 c4 = *reinterpret_cast<const float4*>(ct + pi[0]);
+          const float4 s4 = *reinterpret_cast<const float4*>(st + pi[0]);
+          cs[i][0] = c4.x; cs[i][1] = c4.y; cs[i][2] = c4.z; cs[i][3] = c4.w;
+          sn[i][0] = s4.x; sn[i][1] = s4.y; sn[i][2] = s4.z; sn[i][3] = s4.w;
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            cs[i][k] = rot[k] ? ct[pi[k]] : 1.0f;
+            sn[i][k] = rot[k] ? st[pi[k]] : 0.0f;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cs[i][k] = sn[i][k] = __builtin_nanf("");
+      }
+    }
+  }
+  float sum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  uint16_t* dst_pre = p.dq_pre + (r0 + rg) * p.N + n0;
+  uint8_t* dst_rc = rc ? rc + (r0 + rg) * p.N + n0 : nullptr;
+  uint8_t* dst_rs = rs ? rs + (r0 + rg) * (p.N / 32) + n0 / 32 : nullptr;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool live = FULL || rg + 16 * i < rows;
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float a = bf16_lo(g[i][k]);
+      float b = bf16_hi(g[i][k]);
+      if (any_rot && rot[k]) inv_rotate(a, b, cs[i][k], sn[i][k]);
+      if (db_part) {
+        sum[2 * k] += live ? a : 0.0f;
+        sum[2 * k + 1] += live ? b : 0.0f;
+      }
+      o[k] = live ? pack_bf16x2(a, b) : 0u;
+    }
+    *reinterpret_cast<u32x4_t*>(tile + (rg + 16 * i) * (MXB_COLS / 2) + 4 * chunk) = u32x4_t{o[0], o[1], o[2], o[3]};
+    if (live) *reinterpret_cast<u32x4_t*>(dst_pre + i * step) = u32x4_t{o[0], o[1], o[2], o[3]};
+    if (rc) {
+      // along n from the bf16 copy; the four lanes of the block share its row
+      const uint32_t m = quad_max_u32(packed_bf16_amax<4>(o));
+      uint32_t c0, c1, sc;
+      if (m >= 0x7F800000u) {
+        c0 = c1 = 0x7F7F7F7Fu;
+        sc = 0xFF;
+      } else {
+        const int E = mx_block_exp(m);
+        c0 = e4m3_pack4(bf16_lo(o[0]), bf16_hi(o[0]), bf16_lo(o[1]), bf16_hi(o[1]), E);
+        c1 = e4m3_pack4(bf16_lo(o[2]), bf16_hi(o[2]), bf16_lo(o[3]), bf16_hi(o[3]), E);
+        sc = (uint32_t)(E + 127);
+      }
+      if (live) {
+        *reinterpret_cast<uint2*>(dst_rc + i * step) = make_uint2(c0, c1);
+        if ((chunk & 3) == 0) dst_rs[i * (step / 32)] = (uint8_t)sc;
+      }
+    }
+  }
+  if (db_part) {
+    // the four row groups of a wave (lanes 16 apart) first: every lane ends
+    // with (s0 + s1) + (s2 + s3), whatever its place in the four
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sum[k] += __shfl_xor(sum[k], 16);
+      sum[k] += __shfl_xor(sum[k], 32);
+    }
+    if ((tid & 63) < 16) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) red[tid >> 6][8 * chunk + k] = sum[k];
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2 ----
+  if (db_part && (FULL || rows > 0) && tid < MXB_COLS)
+    db_part[band * p.N + nt0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  if (tc) {
+    const int lane = tid & 63, blk = tid >> 6;
+    // the column pair as 32 packed bf16 words
+    uint32_t wv[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) wv[i] = tile[(32 * blk + i) * (MXB_COLS / 2) + lane];
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      lo = max(lo, wv[i] & 0x7FFFu);
+      hi = max(hi, wv[i] & 0x7FFF0000u);
+    }
+    const int64_t tb = r0 + 32 * blk;  // first token of the block (< Tp)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t m = h ? hi : lo << 16;
+      uint32_t P[8], sc;
+      if (m >= 0x7F800000u) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) P[k] = 0x7F7F7F7Fu;
+        sc = 0xFF;
+      } else {
+        const int E = mx_block_exp(m);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t* q = wv + 4 * k;
+          P[k] = h ? e4m3_pack4(bf16_hi(q[0]), bf16_hi(q[1]), bf16_hi(q[2]), bf16_hi(q[3]), E)
+                   : e4m3_pack4(bf16_lo(q[0]), bf16_lo(q[1]), bf16_lo(q[2]), bf16_lo(q[3]), E);
+        }
+        sc = (uint32_t)(E + 127);
+      }
+      const int64_t col = nt0 + 2 * lane + h;
+      uint8_t* dst = tc + col * Tp + tb;
+      reinterpret_cast<u32x4_t*>(dst)[0] = u32x4_t{P[0], P[1], P[2], P[3]};
+      reinterpret_cast<u32x4_t*>(dst)[1] = u32x4_t{P[4], P[5], P[6], P[7]};
+      ts[col * (Tp / 32) + tb / 32] = (uint8_t)sc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void inv_rope_mx_kernel(BwdParams p, int64_t Tp, float* __restrict__ db_part,
+                                                          uint8_t* __restrict__ rc, uint8_t* __restrict__ rs,
+                                                          uint8_t* __restrict__ tc, uint8_t* __restrict__ ts,
+                                                          int col_tiles) {
+  __shared__ __attribute__((aligned(16))) uint32_t tile[MXB_ROWS * MXB_COLS / 2];  // bf16 pairs
+  __shared__ float red[4][MXB_COLS];  // db: one row of column sums per wave
+  __shared__ int s_pos[MXB_ROWS];
+  // one-dimensional grid, column tile fastest: the workgroups of a band are
+  // dispatched together and read its rows whole
+  const int64_t band = blockIdx.x / (uint32_t)col_tiles;
+  const int64_t r0 = band * MXB_ROWS;
+  const int rows = (int)max((int64_t)0, min((int64_t)MXB_ROWS, p.T - r0));  // 0 for a band of padding only
+  const int nt0 = (int)(blockIdx.x - band * col_tiles) * MXB_COLS;
+  const TokenMap tm{p.fmt, p.B, p.S, p.cu, p.nseq};
+  if (threadIdx.x < MXB_ROWS) {
+    const int i = threadIdx.x;
+    int pos = 0;  // pad rows: any row of the table (their values are dropped)
+    if (i < rows) {
+      int b, s;
+      token_coords(tm, r0 + i, pos, b, s);
+      if (pos < 0 || pos >= p.rope_rows) pos = -1;
+    }
+    s_pos[i] = pos;
+  }
+  __syncthreads();
+  if (rows == MXB_ROWS)
+    mx_pass_band<true>(p, Tp, band, rows, nt0, db_part, rc, rs, tc, ts, tile, red, s_pos);
+  else
+    mx_pass_band<false>(p, Tp, band, rows, nt0, db_part, rc, rs, tc, ts, tile, red, s_pos);
 }
 
 // db[n] = sum of the per-chunk partials in a fixed order: G lanes per column
@@ -747,11 +988,13 @@ hipError_t launch_qup_bwd_mx(const BwdParams& p, const MxBwdPlan& pl, int fp8_mf
   uint8_t* ws = static_cast<uint8_t*>(p.workspace);
   const int64_t T = p.T;
   const int N = p.N, K = p.K;
-  // dq_pre with its quantization along n (the dX operand) and the db partials
-  // in one pass; the quantization along t reads the stored dq_pre below
+  // one pass over dq: dq_pre, its quantizations along n (the dX operand) and
+  // along t (the dW operand, transposed), and the db partials of 64-row bands
   float* db_part = p.use_bias ? reinterpret_cast<float*>(ws + pl.base.db_off) : nullptr;
-  hipLaunchKernelGGL(inv_rope_kernel<true>, dim3((N + IR_COLS - 1) / IR_COLS, pl.base.db_row_chunks),
-                     dim3(IR_THREADS), 0, stream, p, pl.base.ir_rows, db_part, ws + pl.dq_rows, ws + pl.dq_rows_sc);
+  const int col_tiles = (N + MXB_COLS - 1) / MXB_COLS;
+  hipLaunchKernelGGL(inv_rope_mx_kernel, dim3((unsigned)(pl.Tp / MXB_ROWS * col_tiles)), dim3(256), 0, stream, p,
+                     pl.Tp, db_part, p.dx ? ws + pl.dq_rows : nullptr, p.dx ? ws + pl.dq_rows_sc : nullptr,
+                     p.dw ? ws + pl.dq_t : nullptr, p.dw ? ws + pl.dq_t_sc : nullptr, col_tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.use_bias) {
@@ -787,8 +1030,6 @@ hipError_t launch_qup_bwd_mx(const BwdParams& p, const MxBwdPlan& pl, int fp8_mf
     }
   }
   if (p.dw) {
-    if ((e = launch_mxfp8_quantize_t(p.dq_pre, T, N, N, pl.Tp, ws + pl.dq_t, ws + pl.dq_t_sc, stream)))
-      return e;
     if ((e = launch_mxfp8_quantize_t(p.x, T, K, K, pl.Tp, ws + pl.x_t, ws + pl.x_t_sc, stream))) return e;
     FwdParams g{};
     g.x = ws + pl.dq_t;

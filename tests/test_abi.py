@@ -237,12 +237,11 @@ def test_bwd_noalloc_validation(L):
 
 def test_bwd_mxfp8_workspace_and_validation(L):
     # T = 256, N = 4 * 192 = 768, K = 1536: db partials (one column-sum row per
-    # 8-token band: a single 1024-column block leaves the inverse-RoPE grid short
-    # of 1536 workgroups even at 8 rows, the smallest band), then the quantized
+    # 128-token band, the band of the fused pass over dq), then the quantized
     # operands, each 256-byte aligned (all of these sizes already are); dX needs
     # no split here (16 tiles, 6 stages of 128).
     T, N, K = 256, 768, 1536
-    db_part = (T // 8) * N * 4
+    db_part = (T // 128) * N * 4
     expect = db_part + T * N + T * N // 32 + N * T + N * T // 32 + K * N + K * N // 32 \
         + K * T + K * T // 32
     assert L.mla_qup_bwd_mxfp8_workspace_size(ctypes.byref(bwd_args())) == expect

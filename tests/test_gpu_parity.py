@@ -640,6 +640,10 @@ def test_bwd_mxfp8_small_against_oracle(fp8_mfma):
         g = run_bwd(dq, x, w, H=H, dn=128, dr=64, S=T, dw_fp32=dw_fp32, mx=fp8_mfma)
         r = o.qup_backward_mxfp8(dq, x, w, H=H, d_nope=128, d_rope=64, cos=g["oc"], sin=g["os"], S=T)
         _check_mx_bwd(g, r, f"mx bwd fp8_mfma={fp8_mfma} dw_fp32={dw_fp32}", fp8_mfma)
+    # the MXFP8 backward's fused pass over dq rotates exactly as the bf16
+    # backward's inverse RoPE: the same dq_pre, bit for bit (ragged last band)
+    g16 = run_bwd(dq, x, w, H=H, dn=128, dr=64, S=T)
+    assert np.array_equal(bits16(g16["dq_pre"]), bits16(g["dq_pre"]))
 
 
 def test_bwd_mxfp8_thd_dx_only_then_dw_only():
@@ -656,6 +660,46 @@ def test_bwd_mxfp8_thd_dx_only_then_dw_only():
         r = o.qup_backward_mxfp8(dq, x, w, H=H, d_nope=32, d_rope=32, cos=g["oc"], sin=g["os"],
                                  fmt=o.FMT_THD, cu_seqlens=cu.numpy())
         _check_mx_bwd(g, r, f"mx bwd thd {want}")
+
+
+def test_bwd_position_beyond_table_is_nan_in_both_backwards():
+    """A THD sequence longer than the max_seqlen the caller promised, in the
+    backward: both the bf16 backward and the MXFP8 one's fused pass (a whole
+    128-row band and a ragged one) turn the rotated columns of positions past
+    the table into NaN, leave the other columns finite, and agree bit for bit
+    on dq_pre."""
+    lengths = [150, 30]
+    cu = _dev(syn.cu_seqlens_of(lengths))
+    T, K, H, dn, dr = 180, 64, 2, 32, 32
+    N = H * (dn + dr)
+    x = _dev(syn.normal_bf16((T, K), 1.0, 180))
+    w = _dev(syn.normal_bf16((N, K), 0.1, 181))
+    dq = _dev(syn.normal_bf16((T, H, dn + dr), 1e-2, 182))
+    cos = torch.empty(64, dr // 2, device=DEV)
+    sin = torch.empty_like(cos)
+    m.rope_cache_build(cos, sin, dr, 1e4)
+    pres = []
+    for mx in (None, False):
+        dq_pre = torch.empty(T, N, dtype=torch.bfloat16, device=DEV)
+        dx = torch.empty(T, K, dtype=torch.bfloat16, device=DEV)
+        dw = torch.empty(N, K, dtype=torch.float32, device=DEV)
+        kw = dict(H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin, dx=dx, dw=dw, use_bias=False,
+                  fmt=m.FMT_THD, cu_seqlens=cu, max_seqlen=64)
+        if mx is None:
+            n = m.mla_qup_bwd_workspace_size(dq, x, w, dq_pre, **kw)
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+            m.mla_qup_bwd(dq, x, w, dq_pre, workspace=ws if n else None, **kw)
+        else:
+            n = m.mla_qup_bwd_mxfp8_workspace_size(dq, x, w, dq_pre, **kw)
+            ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+            m.mla_qup_bwd_mxfp8(dq, x, w, dq_pre, fp8_mfma=mx, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        pres.append(dq_pre.float().cpu().numpy().reshape(T, H, dn + dr))
+    pos = np.array(list(range(150)) + list(range(30)))
+    for d in pres:
+        assert np.isnan(d[pos >= 64][:, :, dn:]).all()
+        assert np.isfinite(d[pos < 64]).all() and np.isfinite(d[:, :, :dn]).all()
+    assert np.array_equal(pres[0].view(np.uint32), pres[1].view(np.uint32))
 
 
 def test_bwd_mxfp8_zero_tokens_zeroes_dw_db():
