@@ -702,6 +702,65 @@ def test_bwd_position_beyond_table_is_nan_in_both_backwards():
     assert np.array_equal(pres[0].view(np.uint32), pres[1].view(np.uint32))
 
 
+def test_whole_path_replays_bit_identically_from_a_graph():
+    """Graph capture, for serving and training loops that replay a recorded
+    step: the fused forward (MXFP8 BHSD out), the allocation-free backward, the
+    MXFP8 backward (caller's workspace, allocated before capture) and the KV
+    side recorded in one HIP graph. The library makes no allocation, memset or
+    synchronising call on these paths, so capture succeeds; every replay, with
+    eager work and synchronisations between replays, is bit-identical to the
+    eager calls."""
+    T, K, H, dn, dr, dv = 640, 256, 4, 128, 64, 128
+    N = H * (dn + dr)
+    x = _dev(syn.normal_bf16((T, K), 1.0, 190))
+    w = _dev(syn.normal_bf16((N, K), 0.05, 191))
+    dq = _dev(syn.normal_bf16((T, H, dn + dr), 1e-2, 192))
+    kv = _dev(syn.normal_bf16((T, H, dn + dv), 1.0, 193))
+    pe = _dev(syn.normal_bf16((T, dr), 1.0, 194))
+    cos = torch.empty(T, dr // 2, device=DEV)
+    sin = torch.empty_like(cos)
+    m.rope_cache_build(cos, sin, dr, 1e4)
+    u8 = dict(dtype=torch.uint8, device=DEV)
+    b16 = dict(dtype=torch.bfloat16, device=DEV)
+
+    def bufs():
+        return dict(out=torch.empty(1, H, T, dn + dr, **u8), sc=torch.empty(1, H, T, (dn + dr) // 32, **u8),
+                    dq_pre=torch.empty(T, N, **b16), dx=torch.empty(T, K, **b16), dw=torch.empty(N, K, **b16),
+                    db=torch.empty(N, **b16), mdq_pre=torch.empty(T, N, **b16), mdx=torch.empty(T, K, **b16),
+                    mdw=torch.empty(N, K, **b16), key=torch.empty(1, H, T, dn + dr, **u8),
+                    ksc=torch.empty(1, H, T, (dn + dr) // 32, **u8), val=torch.empty(1, H, T, dv, **u8),
+                    vsc=torch.empty(1, H, T, dv // 32, **u8))
+
+    rope = dict(H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin, B=1, S=T)
+    probe = bufs()
+    nws = m.mla_qup_bwd_mxfp8_workspace_size(dq, x, w, probe["mdq_pre"], dx=probe["mdx"], dw=probe["mdw"], **rope)
+    ws = torch.empty(nws, **u8)
+
+    def run(b):
+        m.mla_qup_fwd(x, w, b["out"], out_scales=b["sc"], **rope)
+        m.mla_qup_bwd_noalloc(dq, x, w, b["dq_pre"], dx=b["dx"], dw=b["dw"], db=b["db"], use_bias=True, **rope)
+        m.mla_qup_bwd_mxfp8(dq, x, w, b["mdq_pre"], dx=b["mdx"], dw=b["mdw"], workspace=ws, fp8_mfma=False,
+                            **rope)
+        m.mla_kv_rope(kv, pe, b["key"], b["val"], d_v=dv, key_scales=b["ksc"], value_scales=b["vsc"], **rope)
+
+    ref = bufs()
+    run(ref)  # eager (also the allocation-free entry point's one-time set-up)
+    torch.cuda.synchronize()
+    got = bufs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(got)
+    for rep in range(3):
+        for t in got.values():
+            t.view(torch.uint8).fill_(0xA5 ^ rep)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(got[k].view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
+    assert torch.isfinite(ref["dx"].float()).all() and torch.isfinite(ref["mdw"].float()).all()
+
+
 def test_bwd_mxfp8_zero_tokens_zeroes_dw_db():
     K, H = 64, 2
     x = torch.empty(0, K, dtype=torch.bfloat16, device=DEV)
