@@ -138,7 +138,8 @@ MLA_API mla_status rope_cache_build(float* cos, float* sin, int32_t rows, int32_
  * scale 0xFF and codes 0x7F.
  *   x      : device, x_dtype MLA_DTYPE_BF16 or MLA_DTYPE_FP32, element (r, c)
  *            at x[r*ld + c]; 16-byte aligned, ld*elemsize a multiple of 16.
- *   rows, cols: rows >= 0, cols > 0 and a multiple of 32; ld >= cols.
+ *   rows, cols: rows >= 0, cols > 0 and a multiple of 32, rows * cols <= 2^36;
+ *               ld >= cols.
  *   codes  : device uint8[rows*cols] (row-major, stride cols), 8-byte aligned.
  *   scales : device uint8[rows*cols/32] (row-major, stride cols/32).
  * Errors: MLA_EINVAL, MLA_EALIAS. */

@@ -189,7 +189,9 @@ mla_status mxfp8_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t 
   size_t es = x_dtype == MLA_DTYPE_FP32 ? 4 : 2;
   if (!aligned(x, 16) || ((size_t)ld * es) % 16 != 0 || !aligned(codes, 8)) return MLA_EINVAL;
   if (rows > ((int64_t)1 << 40) || cols > ((int64_t)1 << 31)) return MLA_EINVAL;
-  if (rows > (((int64_t)1 << 43) / cols)) return MLA_EINVAL;  // rows * cols <= 2^43 (grid size)
+  // rows * cols <= 2^36: one launch of rows * cols / 8192 workgroups of 256
+  // threads stays within the 2^32 work-items of a grid dimension
+  if (rows > (((int64_t)1 << 36) / cols)) return MLA_EINVAL;
   size_t xbytes = ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * es;
   if (overlaps({rng(codes, (size_t)rows * cols), rng(scales, (size_t)rows * cols / 32)},
                {rng(x, xbytes)}))

@@ -9,6 +9,8 @@
 // (one 16-byte bf16 load or two fp32 loads per lane, one 8-byte store); the
 // block amax is an integer max over |x| bit patterns reduced across the four
 // lanes with two xor-shuffles.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -108,52 +110,59 @@ __global__ __launch_bounds__(256) void mxfp8_quant_t_kernel(const uint16_t* __re
                                                             uint8_t* __restrict__ scales_t) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[QT_ROWS * 128];
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * QT_ROWS;
   const int64_t c0 = (int64_t)blockIdx.y * QT_COLS;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 32 * j + (tid >> 3), chunk = tid & 7;
-    const int64_t r = r0 + row, c = c0 + 8 * chunk;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < rows && c < cols) v = *reinterpret_cast<const uint4*>(x + r * ld + c);
-    *reinterpret_cast<uint4*>(tile + row * 128 + ((chunk ^ (2 * j)) << 4)) = v;
-  }
-  __syncthreads();
   const int lane = tid & 63, wave = tid >> 6;
   const int cl = 16 * wave + (lane >> 2), b = lane & 3;
-  const int64_t c = c0 + cl, rb = r0 + 32 * b;
-  if (c >= cols || rb >= rows_pad) return;
-  const uint8_t* col = tile + ((((cl >> 3) ^ (2 * b)) << 4) + 2 * (cl & 7)) + 32 * b * 128;
-  float v[32];
-  uint32_t m = 0;
+  const int64_t c = c0 + cl;
+  const int64_t row_tiles = (rows_pad + QT_ROWS - 1) / QT_ROWS;
+  // row tiles grid-strided (the launch caps the grid's x extent)
+  for (int64_t rt = blockIdx.x; rt < row_tiles; rt += gridDim.x) {
+    const int64_t r0 = rt * QT_ROWS;
+    __syncthreads();  // the previous tile's readers are done
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    v[i] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(col + i * 128));
-    m = max(m, abs_bits(v[i]));
+    for (int j = 0; j < 4; ++j) {
+      const int row = 32 * j + (tid >> 3), chunk = tid & 7;
+      const int64_t r = r0 + row, cc = c0 + 8 * chunk;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < rows && cc < cols) v = *reinterpret_cast<const uint4*>(x + r * ld + cc);
+      *reinterpret_cast<uint4*>(tile + row * 128 + ((chunk ^ (2 * j)) << 4)) = v;
+    }
+    __syncthreads();
+    const int64_t rb = r0 + 32 * b;
+    if (c >= cols || rb >= rows_pad) continue;
+    const uint8_t* col = tile + ((((cl >> 3) ^ (2 * b)) << 4) + 2 * (cl & 7)) + 32 * b * 128;
+    float v[32];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      v[i] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(col + i * 128));
+      m = max(m, abs_bits(v[i]));
+    }
+    uint32_t P[8];
+    uint32_t sc;
+    if (m >= 0x7F800000u) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) P[k] = 0x7F7F7F7Fu;
+      sc = 0xFF;
+    } else {
+      const int E = mx_block_exp(m);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) P[k] = e4m3_pack4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3], E);
+      sc = (uint32_t)(E + 127);
+    }
+    uint8_t* dst = codes_t + c * rows_pad + rb;
+    reinterpret_cast<u32x4_t*>(dst)[0] = u32x4_t{P[0], P[1], P[2], P[3]};
+    reinterpret_cast<u32x4_t*>(dst)[1] = u32x4_t{P[4], P[5], P[6], P[7]};
+    scales_t[c * (rows_pad / 32) + rb / 32] = (uint8_t)sc;
   }
-  uint32_t P[8];
-  uint32_t sc;
-  if (m >= 0x7F800000u) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) P[k] = 0x7F7F7F7Fu;
-    sc = 0xFF;
-  } else {
-    const int E = mx_block_exp(m);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) P[k] = e4m3_pack4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3], E);
-    sc = (uint32_t)(E + 127);
-  }
-  uint8_t* dst = codes_t + c * rows_pad + rb;
-  reinterpret_cast<u32x4_t*>(dst)[0] = u32x4_t{P[0], P[1], P[2], P[3]};
-  reinterpret_cast<u32x4_t*>(dst)[1] = u32x4_t{P[4], P[5], P[6], P[7]};
-  scales_t[c * (rows_pad / 32) + rb / 32] = (uint8_t)sc;
 }
 
 }  // namespace
 
 hipError_t launch_mxfp8_quantize_t(const void* x, int64_t rows, int64_t cols, int64_t ld, int64_t rows_pad,
                                    uint8_t* codes_t, uint8_t* scales_t, hipStream_t stream) {
-  const dim3 grid((unsigned)((rows_pad + QT_ROWS - 1) / QT_ROWS), (unsigned)((cols + QT_COLS - 1) / QT_COLS));
+  const int64_t row_tiles = (rows_pad + QT_ROWS - 1) / QT_ROWS;
+  const dim3 grid((unsigned)std::min<int64_t>(row_tiles, 1 << 16), (unsigned)((cols + QT_COLS - 1) / QT_COLS));
   hipLaunchKernelGGL(mxfp8_quant_t_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x), rows,
                      cols, ld, rows_pad, codes_t, scales_t);
   return hipGetLastError();

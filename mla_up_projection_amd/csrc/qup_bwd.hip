@@ -46,29 +46,20 @@ __device__ __forceinline__ void inv_rotate(float& a, float& b, float c, float s)
   b = nb;
 }
 
-// RQ: also quantize each dq_pre row along n from its bf16 copy (the MXFP8
-// backward's dX operand): the four lanes of a 32-column block share its amax
-// through two xor-shuffles; codes [T, N] and scales [T, N/32].
-template <bool RQ>
-__global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, int band, float* __restrict__ db_part,
-                                                              uint8_t* __restrict__ rc, uint8_t* __restrict__ rs) {
+// Bands of `band` token rows (at most IR_ROWS) are strided over the grid's y
+// extent, which the launch caps; each band's column sums go to its own db
+// partial row.
+__global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, int band, int64_t bands,
+                                                              float* __restrict__ db_part) {
   __shared__ int s_pos[IR_ROWS];
-  const int64_t r0 = (int64_t)blockIdx.y * band;  // band <= IR_ROWS token rows
-  const int rows = (int)min((int64_t)band, p.T - r0);
   const TokenMap tm{p.fmt, p.B, p.S, p.cu, p.nseq};
-  for (int i = threadIdx.x; i < rows; i += IR_THREADS) {
-    int pos, b, s;
-    token_coords(tm, r0 + i, pos, b, s);
-    s_pos[i] = pos;
-  }
-  __syncthreads();
   const int n0 = blockIdx.x * IR_COLS + threadIdx.x * 8;
-  if (n0 >= p.N) return;
+  const bool col_ok = n0 < p.N;
   const uint16_t* __restrict__ dq = p.dq;
   uint16_t* __restrict__ dq_pre = p.dq_pre;
   const float* __restrict__ cos_t = p.cos;
   const float* __restrict__ sin_t = p.sin;
-  const int d0 = n0 % p.D;  // 8 consecutive columns stay inside one head
+  const int d0 = (col_ok ? n0 : 0) % p.D;  // 8 consecutive columns stay inside one head
   bool rot[4];
   int pi[4];
 #pragma unroll
@@ -81,86 +72,72 @@ __global__ __launch_bounds__(IR_THREADS) void inv_rope_kernel(BwdParams p, int b
   // all four pairs rotated and their table entries 16-byte aligned: one
   // float4 of cos and one of sin per row
   const bool vec4 = rot[0] && rot[3] && (pi[0] & 3) == 0 && (p.rope_pairs & 3) == 0;
-  float sum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  // Rows in batches of RB: all loads of a batch are issued before any store,
-  // so RB 16-byte loads per lane are in flight at once. dq is read exactly
-  // once (non-temporal load); dq_pre is read again by the GEMMs.
-  constexpr int RB = 8;
-  for (int i0 = 0; i0 < rows; i0 += RB) {
-    u32x4_t g[RB];
-    float cs[RB][4], sn[RB][4];
+  for (int64_t bi = blockIdx.y; bi < bands; bi += gridDim.y) {
+    const int64_t r0 = bi * band;
+    const int rows = (int)min((int64_t)band, p.T - r0);
+    __syncthreads();  // the previous band's readers of s_pos are done
+    for (int i = threadIdx.x; i < rows; i += IR_THREADS) {
+      int pos, b, s;
+      token_coords(tm, r0 + i, pos, b, s);
+      s_pos[i] = pos;
+    }
+    __syncthreads();
+    if (!col_ok) continue;
+    float sum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // Rows in batches of RB: all loads of a batch are issued before any
+    // store, so RB 16-byte loads per lane are in flight at once. dq is read
+    // exactly once (non-temporal load); dq_pre is read again by the GEMMs.
+    constexpr int RB = 8;
+    for (int i0 = 0; i0 < rows; i0 += RB) {
+      u32x4_t g[RB];
+      float cs[RB][4], sn[RB][4];
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int i = i0 + j < rows ? i0 + j : rows - 1;
-      g[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(dq + (r0 + i) * p.N + n0));
-      if (any_rot) {
-        const int pos = s_pos[i];
-        const bool pos_ok = pos >= 0 && pos < p.rope_rows;
-        const int64_t trow = (int64_t)(pos_ok ? pos : 0) * p.rope_pairs;
-        if (vec4) {
-          const float4 c4 = *reinterpret_cast<const float4*>(cos_t + trow + pi[0]);
-          const float4 s4 = *reinterpret_cast<const float4*>(sin_t + trow + pi[0]);
-          cs[j][0] = c4.x; cs[j][1] = c4.y; cs[j][2] = c4.z; cs[j][3] = c4.w;
-          sn[j][0] = s4.x; sn[j][1] = s4.y; sn[j][2] = s4.z; sn[j][3] = s4.w;
-        } else {
+      for (int j = 0; j < RB; ++j) {
+        const int i = i0 + j < rows ? i0 + j : rows - 1;
+        g[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(dq + (r0 + i) * p.N + n0));
+        if (any_rot) {
+          const int pos = s_pos[i];
+          const bool pos_ok = pos >= 0 && pos < p.rope_rows;
+          const int64_t trow = (int64_t)(pos_ok ? pos : 0) * p.rope_pairs;
+          if (vec4) {
+            const float4 c4 = *reinterpret_cast<const float4*>(cos_t + trow + pi[0]);
+            const float4 s4 = *reinterpret_cast<const float4*>(sin_t + trow + pi[0]);
+            cs[j][0] = c4.x; cs[j][1] = c4.y; cs[j][2] = c4.z; cs[j][3] = c4.w;
+            sn[j][0] = s4.x; sn[j][1] = s4.y; sn[j][2] = s4.z; sn[j][3] = s4.w;
+          } else {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            cs[j][k] = rot[k] ? cos_t[trow + pi[k]] : 1.0f;
-            sn[j][k] = rot[k] ? sin_t[trow + pi[k]] : 0.0f;
+            for (int k = 0; k < 4; ++k) {
+              cs[j][k] = rot[k] ? cos_t[trow + pi[k]] : 1.0f;
+              sn[j][k] = rot[k] ? sin_t[trow + pi[k]] : 0.0f;
+            }
+          }
+          if (!pos_ok) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) cs[j][k] = sn[j][k] = __builtin_nanf("");
           }
         }
-        if (!pos_ok) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) cs[j][k] = sn[j][k] = __builtin_nanf("");
-        }
       }
-    }
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      if (i0 + j >= rows) break;
-      uint32_t o[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float a = bf16_bits_to_f32(g[j][k] & 0xFFFFu);
-        float b = bf16_bits_to_f32(g[j][k] >> 16);
-        if (any_rot && rot[k]) inv_rotate(a, b, cs[j][k], sn[j][k]);
-        sum[2 * k] += a;
-        sum[2 * k + 1] += b;
-        o[k] = pack_bf16x2(a, b);
-      }
-      *reinterpret_cast<u32x4_t*>(dq_pre + (r0 + i0 + j) * p.N + n0) = u32x4_t{o[0], o[1], o[2], o[3]};
-      if (RQ) {
-        float v[8];
+      for (int j = 0; j < RB; ++j) {
+        if (i0 + j >= rows) break;
+        uint32_t o[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          v[2 * k] = bf16_bits_to_f32(o[k] & 0xFFFFu);
-          v[2 * k + 1] = bf16_bits_to_f32(o[k] >> 16);
+          float a = bf16_bits_to_f32(g[j][k] & 0xFFFFu);
+          float b = bf16_bits_to_f32(g[j][k] >> 16);
+          if (any_rot && rot[k]) inv_rotate(a, b, cs[j][k], sn[j][k]);
+          sum[2 * k] += a;
+          sum[2 * k + 1] += b;
+          o[k] = pack_bf16x2(a, b);
         }
-        uint32_t m = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) m = max(m, abs_bits(v[k]));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-        uint32_t c0, c1, sc;
-        if (m >= 0x7F800000u) {
-          c0 = c1 = 0x7F7F7F7Fu;
-          sc = 0xFF;
-        } else {
-          const int E = mx_block_exp(m);
-          c0 = e4m3_pack4(v[0], v[1], v[2], v[3], E);
-          c1 = e4m3_pack4(v[4], v[5], v[6], v[7], E);
-          sc = (uint32_t)(E + 127);
-        }
-        const int64_t row = r0 + i0 + j;
-        *reinterpret_cast<uint2*>(rc + row * p.N + n0) = make_uint2(c0, c1);
-        if ((threadIdx.x & 3) == 0) rs[row * (p.N / 32) + n0 / 32] = (uint8_t)sc;
+        *reinterpret_cast<u32x4_t*>(dq_pre + (r0 + i0 + j) * p.N + n0) = u32x4_t{o[0], o[1], o[2], o[3]};
       }
     }
-  }
-  if (db_part) {
-    float* dst = db_part + (int64_t)blockIdx.y * p.N + n0;
-    reinterpret_cast<float4*>(dst)[0] = make_float4(sum[0], sum[1], sum[2], sum[3]);
-    reinterpret_cast<float4*>(dst)[1] = make_float4(sum[4], sum[5], sum[6], sum[7]);
+    if (db_part) {
+      float* dst = db_part + bi * p.N + n0;
+      reinterpret_cast<float4*>(dst)[0] = make_float4(sum[0], sum[1], sum[2], sum[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(sum[4], sum[5], sum[6], sum[7]);
+    }
   }
 }
 
@@ -850,17 +827,28 @@ int bg_grid(const BGemm& g, int cus) {
 template <bool F32OUT>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int splits,
                                                           int64_t n4, void* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  float4 s = reinterpret_cast<const float4*>(part)[i];
-  for (int z = 1; z < splits; ++z) {
-    const float4 v = reinterpret_cast<const float4*>(part + (int64_t)z * n4 * 4)[i];
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    float4 s = reinterpret_cast<const float4*>(part)[i];
+    for (int z = 1; z < splits; ++z) {
+      const float4 v = reinterpret_cast<const float4*>(part + (int64_t)z * n4 * 4)[i];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    if (F32OUT)
+      reinterpret_cast<float4*>(out)[i] = s;
+    else
+      reinterpret_cast<uint2*>(out)[i] = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
   }
-  if (F32OUT)
-    reinterpret_cast<float4*>(out)[i] = s;
+}
+
+// n4 groups of four values; the grid is capped and strided.
+hipError_t launch_split_reduce(const float* part, int splits, int64_t n4, void* out, bool f32out,
+                               hipStream_t stream) {
+  const dim3 grid((unsigned)std::min<int64_t>((n4 + 255) / 256, (int64_t)1 << 20));
+  if (f32out)
+    hipLaunchKernelGGL(split_reduce_kernel<true>, grid, dim3(256), 0, stream, part, splits, n4, out);
   else
-    reinterpret_cast<uint2*>(out)[i] = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+    hipLaunchKernelGGL(split_reduce_kernel<false>, grid, dim3(256), 0, stream, part, splits, n4, out);
+  return hipGetLastError();
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int64_t words) {
@@ -888,9 +876,9 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
   }
   float* db_part = p.use_bias ? reinterpret_cast<float*>(ws + pl.db_off) : nullptr;
   {
-    dim3 grid((p.N + IR_COLS - 1) / IR_COLS, pl.db_row_chunks);
-    hipLaunchKernelGGL(inv_rope_kernel<false>, grid, dim3(IR_THREADS), 0, stream, p, pl.ir_rows, db_part, nullptr,
-                       nullptr);
+    dim3 grid((p.N + IR_COLS - 1) / IR_COLS, (unsigned)std::min(pl.db_row_chunks, 65535));
+    hipLaunchKernelGGL(inv_rope_kernel, grid, dim3(IR_THREADS), 0, stream, p, pl.ir_rows,
+                       (int64_t)pl.db_row_chunks, db_part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -927,10 +915,7 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (split) {
-      const int64_t n4 = p.T * p.K / 4;
-      hipLaunchKernelGGL(split_reduce_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                         static_cast<const float*>(g.out), g.splits, n4, p.dx);
-      e = hipGetLastError();
+      e = launch_split_reduce(static_cast<const float*>(g.out), g.splits, p.T * p.K / 4, p.dx, false, stream);
       if (e != hipSuccess) return e;
     }
   }
@@ -957,15 +942,8 @@ hipError_t launch_qup_bwd(const BwdParams& p, const BwdPlan& pl, hipStream_t str
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (split) {
-      const int64_t n4 = (int64_t)p.N * p.K / 4;
-      const dim3 rg((unsigned)((n4 + 255) / 256));
-      if (p.dw_fp32)
-        hipLaunchKernelGGL(split_reduce_kernel<true>, rg, dim3(256), 0, stream,
-                           static_cast<const float*>(g.out), g.splits, n4, p.dw);
-      else
-        hipLaunchKernelGGL(split_reduce_kernel<false>, rg, dim3(256), 0, stream,
-                           static_cast<const float*>(g.out), g.splits, n4, p.dw);
-      e = hipGetLastError();
+      e = launch_split_reduce(static_cast<const float*>(g.out), g.splits, (int64_t)p.N * p.K / 4, p.dw,
+                              p.dw_fp32 != 0, stream);
       if (e != hipSuccess) return e;
     }
   }
@@ -1023,10 +1001,9 @@ hipError_t launch_qup_bwd_mx(const BwdParams& p, const MxBwdPlan& pl, int fp8_mf
     g.out = split ? static_cast<void*>(ws + pl.dx_part) : static_cast<void*>(p.dx);
     if ((e = launch_mx_gemm(g, stream))) return e;
     if (split) {
-      const int64_t n4 = T * K / 4;
-      hipLaunchKernelGGL(split_reduce_kernel<false>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                         reinterpret_cast<const float*>(ws + pl.dx_part), pl.dx_splits, n4, p.dx);
-      if ((e = hipGetLastError())) return e;
+      if ((e = launch_split_reduce(reinterpret_cast<const float*>(ws + pl.dx_part), pl.dx_splits, T * K / 4, p.dx,
+                                   false, stream)))
+        return e;
     }
   }
   if (p.dw) {

@@ -153,6 +153,8 @@ int main() {
   EXPECT(mxfp8_quantize(A(1), MLA_DTYPE_BF16, 8192, 1536, 1536, (uint8_t*)A(2), (uint8_t*)A(3), nullptr), MLA_OK);
   EXPECT(mxfp8_quantize(A(1), MLA_DTYPE_FP32, (int64_t)1 << 41, 64, 64, (uint8_t*)A(2), (uint8_t*)A(3), nullptr), MLA_EINVAL);
   EXPECT(mxfp8_quantize(A(1), MLA_DTYPE_BF16, 4, (int64_t)1 << 40, (int64_t)1 << 40, (uint8_t*)A(2), (uint8_t*)A(3), nullptr), MLA_EINVAL);
+  // 2^37 elements: more work-items than one grid dimension holds
+  EXPECT(mxfp8_quantize(A(1), MLA_DTYPE_BF16, (int64_t)1 << 20, (int64_t)1 << 17, (int64_t)1 << 17, (uint8_t*)A(2), (uint8_t*)A(3), nullptr), MLA_EINVAL);
   EXPECT(mxfp8_quantize_t(A(1), 4096, 24576, 24576, 4096, (uint8_t*)A(2), (uint8_t*)A(3), nullptr), MLA_OK);
   EXPECT(mxfp8_quantize_t(A(1), 4096, 24576, 24576, (int64_t)1 << 41, (uint8_t*)A(2), (uint8_t*)A(3), nullptr), MLA_EINVAL);
   mla_yarn y = {40.0, 4096, 32.0, 1.0, 1.0};

@@ -606,6 +606,22 @@ def test_mxfp8_quantize_t_bitexact():
     assert np.array_equal(scales.cpu().numpy(), rs)
 
 
+def test_mxfp8_quantize_t_more_row_tiles_than_one_grid_column_holds():
+    """8,388,648 rows padded to 8,388,672: 65,537 tiles of 128 rows, past the
+    launch's cap on the grid along the rows, so a workgroup quantizes two
+    tiles; every code and scale against the oracle."""
+    R, C = (1 << 23) + 40, 16
+    Rp = (R + 31) // 32 * 32
+    x = syn.normal_bf16((R, C), 1.0, 151)
+    codes = torch.full((C, Rp), 0xAA, dtype=torch.uint8, device=DEV)
+    scales = torch.full((C, Rp // 32), 0xAA, dtype=torch.uint8, device=DEV)
+    m.mxfp8_quantize_t(_dev(x), codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = o.mxfp8_quantize_columns(o.to_f64(x))
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
 def _check_mx_bwd(g, r, what, fp8_mfma=False):
     """The dequantized operand products are exact in float32, so the only
     error against the oracle is float32 accumulation (far below 1e-6 here),
@@ -759,6 +775,43 @@ def test_whole_path_replays_bit_identically_from_a_graph():
         for k in ref:
             assert torch.equal(got[k].view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
     assert torch.isfinite(ref["dx"].float()).all() and torch.isfinite(ref["mdw"].float()).all()
+
+
+def test_bwd_more_token_bands_than_one_grid_column_holds():
+    """4,196,000 tokens (4196 sequences of 1000) of one 64-wide head: 65,563
+    inverse-RoPE bands of 64 rows, more than the launch's grid extent along
+    the bands (65,535), so workgroups take several bands each, the last one
+    ragged. dq_pre on rows from each end and around the grid's wrap, and db
+    over every token, against the oracle."""
+    B, S, K, H, dn, dr = 4196, 1000, 32, 1, 32, 32
+    T, N = B * S, H * (dn + dr)
+    print(f"\nbackward T={T} N={N}: running", flush=True)
+    dq = syn.normal_bf16((T, H, dn + dr), 1e-2, 200)
+    x = _dev(syn.normal_bf16((T, K), 1.0, 201))
+    w = _dev(syn.normal_bf16((N, K), 0.1, 202))
+    cos, sin, oc, os_ = rope_tables(S, dr)
+    dqd = _dev(dq)
+    dq_pre = torch.empty(T, N, dtype=torch.bfloat16, device=DEV)
+    dw = torch.empty(N, K, dtype=torch.float32, device=DEV)
+    db = torch.empty(N, dtype=torch.bfloat16, device=DEV)
+    kw = dict(H=H, d_nope=dn, d_rope=dr, cos=cos, sin=sin, dw=dw, db=db, use_bias=True, B=B, S=S)
+    n = m.mla_qup_bwd_workspace_size(dqd, x, w, dq_pre, **kw)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    m.mla_qup_bwd(dqd, x, w, dq_pre, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    pos = np.arange(T, dtype=np.int64) % S
+    # db over every token, in chunks of the oracle's inverse rotation
+    ref_db = np.zeros(N)
+    dqf = o.to_f64(dq)
+    for c0 in range(0, T, 1 << 20):
+        c1 = min(T, c0 + (1 << 20))
+        ref_db += o.rope_rotate(dqf[c0:c1], pos[c0:c1], oc, os_, dn, dr, inverse=True).reshape(c1 - c0, N).sum(0)
+    assert frob_rel(o.to_f64(db.cpu()), ref_db) <= 1e-2
+    rows = np.concatenate([np.arange(0, 256), np.arange(65535 * 64 - 256, 65535 * 64 + 256), np.arange(T - 256, T)])
+    ref = o.rope_rotate(dqf[rows], pos[rows], oc, os_, dn, dr, inverse=True).reshape(len(rows), N)
+    got = dq_pre[torch.from_numpy(rows).to(DEV)]
+    check_bf16(bits16(got), o.f32_to_bf16_bits(ref.astype(np.float32)), "dq_pre")
+    assert torch.isfinite(dw).all()
 
 
 def test_bwd_mxfp8_zero_tokens_zeroes_dw_db():
