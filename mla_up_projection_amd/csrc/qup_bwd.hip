@@ -18,6 +18,9 @@
 //                     LDS transpose read (ds_read_b64_tr_b16).
 //   split_reduce_kernel: ordered sum of the reduction splits of dX (long N)
 //                     or dW (few heads, long T) -> bf16 or fp32.
+//   inv_rope_mx_kernel: the MXFP8 backward's one pass over dq: dq_pre, its
+//                     codes along n and along the tokens (transposed), and
+//                     the db partials.
 //   launch_qup_bwd_mx: the MXFP8 backward (operands quantized along each
 //                     product's reduction axis, products on the forward
 //                     kernel's MXFP8 main loop).
