@@ -970,9 +970,11 @@ hipError_t launch_qup_bwd_mx(const BwdParams& p, const MxBwdPlan& pl, int fp8_mf
   const int64_t T = p.T;
   const int N = p.N, K = p.K;
   // one pass over dq: dq_pre, its quantizations along n (the dX operand) and
-  // along t (the dW operand, transposed), and the db partials of 64-row bands
+  // along t (the dW operand, transposed), and the db partials of 128-row
+  // bands; the pass assumes whole 128-column tiles and bands
+  if (N % MXB_COLS != 0 || pl.Tp % MXB_ROWS != 0 || pl.base.ir_rows != MXB_ROWS) return hipErrorInvalidValue;
   float* db_part = p.use_bias ? reinterpret_cast<float*>(ws + pl.base.db_off) : nullptr;
-  const int col_tiles = (N + MXB_COLS - 1) / MXB_COLS;
+  const int col_tiles = N / MXB_COLS;
   hipLaunchKernelGGL(inv_rope_mx_kernel, dim3((unsigned)(pl.Tp / MXB_ROWS * col_tiles)), dim3(256), 0, stream, p,
                      pl.Tp, db_part, p.dx ? ws + pl.dq_rows : nullptr, p.dx ? ws + pl.dq_rows_sc : nullptr,
                      p.dw ? ws + pl.dq_t : nullptr, p.dw ? ws + pl.dq_t_sc : nullptr, col_tiles);
