@@ -678,6 +678,24 @@ def test_bwd_mxfp8_thd_dx_only_then_dw_only():
         _check_mx_bwd(g, r, f"mx bwd thd {want}")
 
 
+@pytest.mark.parametrize("want", [("dx",), ("dw",), ("dx", "dw")])
+def test_bwd_mxfp8_sbhd_yarn_bias(want):
+    """SBHD tokens (3 sequences of 111: three bands, the last ragged), a YaRN
+    table and the bias gradient through the MXFP8 backward's fused pass, with
+    dX only, dW only and both."""
+    B, S, K, H = 3, 111, 128, 2
+    T = B * S
+    x = syn.normal_bf16((T, K), 1.0, 175)
+    w = syn.normal_bf16((H * 192, K), 0.03, 176)
+    dq = syn.normal_bf16((T, H, 192), 1e-2, 177)
+    yarn = (40.0, 64, 32.0, 1.0, 1.0)
+    g = run_bwd(dq, x, w, H=H, dn=128, dr=64, fmt=m.FMT_SBHD, B=B, S=S, use_bias=True, yarn=yarn,
+                mx=False, want=want)
+    r = o.qup_backward_mxfp8(dq, x, w, H=H, d_nope=128, d_rope=64, cos=g["oc"], sin=g["os"],
+                             fmt=o.FMT_SBHD, B=B, S=S)
+    _check_mx_bwd(g, r, f"mx bwd sbhd yarn bias {want}")
+
+
 def test_bwd_position_beyond_table_is_nan_in_both_backwards():
     """A THD sequence longer than the max_seqlen the caller promised, in the
     backward: both the bf16 backward and the MXFP8 one's fused pass (a whole
